@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Benchmark: GEMM throughput (TFLOP/s) of the HIP library on one MI355X.
+
+One step = one call of the library (argument checks, tile-config choice,
+one kernel launch) over the resident inputs of the workload.  Default
+workload: the 8192^3 bf16 NN product with bf16 output (A, B ~ N(0, 1),
+seed 4).  The 4096^3 fp16 NN product is measured alongside (its figure is
+reported under "also").  Inputs are generated on the host, copied to HBM
+before timing, and stay there.
+
+Prints ONE JSON line.  Timing: W untimed warm-up steps; then K timed steps
+between two device synchronisations (wall clock -> ms_per_step and value),
+with a HIP event pair around every launch on the stream the kernel runs on
+(-> the kernel's average duration for the roofline figure).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at 4096³ and 8192³ fp16 (fraction of MFMA peak), 1 MI355X"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16 MFMA, published
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counters are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_gemm_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, or None if absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_workload(tdg, torch, w, steps, warmup):
+    from workloads import TORCH_DTYPE, workload_inputs
+    a, b = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    a, b = a.to(dev), b.to(dev)
+    out_dt = TORCH_DTYPE[w.out_dtype]
+    shape = (w.batch, w.M, w.N) if w.batch else (w.M, w.N)
+    c = torch.empty(shape, dtype=out_dt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        tdg.gemm(a, b, layout=w.layout, out=c)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        tdg.gemm(a, b, layout=w.layout, out=c)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
+    return wall * 1e3 / steps, kernel_ms, tdg.tdg_config_name(cfg)
+
+
+def cpu_baseline(w, seconds_target=15.0):
+    """The oracle, unchanged, on a bounded row sample of the same workload."""
+    import numpy as np
+    from oracle import oracle
+    from workloads import bits, workload_inputs
+    a, b = workload_inputs(w)
+    ab, bb = bits(a), bits(b)
+    nt = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        nt = min(nt, int(omp))
+    # calibrate on a few rows, then size the sample to ~seconds_target
+    probe = np.arange(0, w.M, max(1, w.M // 8), dtype=np.int64)[:8]
+    t0 = time.perf_counter()
+    oracle.gemm(ab, bb, w.in_dtype, w.layout, rows=probe, nthreads=nt)
+    t_probe = time.perf_counter() - t0
+    per_row = t_probe / len(probe)
+    nrows = int(max(8, min(w.M, seconds_target / max(per_row, 1e-9))))
+    rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm(ab, bb, w.in_dtype, w.layout, rows=rows, nthreads=nt)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+            "sample": "%d of %d output rows (all %d columns, full K=%d), %.1f s; value = 2*rows*N*K / time"
+                      % (len(rows), w.M, w.N, w.K, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="nn_bf16_8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU; --gpus %d is not offered (the product shards "
+              "with no exchange over output tiles, see the design notes)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_dense_gemm_03_amd as tdg
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    ms, kernel_ms, cfg_name = time_workload(tdg, torch, w, args.steps, args.warmup)
+    flops = w.flops
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    traffic = stored_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
+                   "batch": w.batch, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype, "accumulate": "f32",
+                   "inputs": "%s seed %d" % (w.dist, w.seed), "tile_config": cfg_name,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_ms": round(kernel_ms, 5)},
+    }
+    if not args.no_also:
+        also = []
+        for name in ("nn_f16_4096",):
+            if name == w.name:
+                continue
+            wa = WORKLOADS[name]
+            ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup)
+            also.append({"workload": name, "value": round(wa.flops / (ms_a * 1e-3) / 1e12, 2),
+                         "kernel_tflops": round(wa.flops / (kms_a * 1e-3) / 1e12, 2),
+                         "frac": round(wa.flops / (kms_a * 1e-3) / 1e12 / PEAK_TFLOPS[wa.in_dtype], 4),
+                         "ms_per_step": round(ms_a, 5), "tile_config": cfg_a})
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * tdg.h -- tiled dense GEMM for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * Operation.  C = A * B ("NN", B stored K x N) or C = A * B^T ("TN", B stored
+ * N x K), with fp16 or bf16 inputs, fp32 accumulation and fp16, bf16 or fp32
+ * output.  Every output element is the full sum over K of products of input
+ * elements:  C[i,j] = sum_{p<K} A[i,p] * Bt[p,j].
+ *   - The product, its tile decomposition, the zero-filled reads past the
+ *     matrix edges and the store mask of edge tiles follow the NineToothed
+ *     GEMM primer (studypath task3 appendix), sections 3 (index map),
+ *     4 (M and N over the grid, K as a loop inside one program) and
+ *     5 (tail tiles: masked reads return 0, masked store).
+ *   - The TN form is the [N, K] right operand of the warp-level kernel in the
+ *     Croqtile tutorial, chapter 4 ("tensor contraction: mma syntax"),
+ *     read as out[m,n] = sum_k lhs[m,k] * rhs[n,k].
+ *   - fp32 accumulation follows section 6 of the NineToothed primer; the
+ *     fp32 -> fp16/bf16 output conversion rounds to nearest even, overflow
+ *     to +-inf.
+ *
+ * Layout.  All matrices are row-major.  Leading dimensions are row strides
+ * in ELEMENTS: lda >= K; ldb >= N (NN) or ldb >= K (TN); ldc >= N.  Batched
+ * calls add element strides between consecutive problems (strideA/B/C); the
+ * problems are independent.  Any pointer alignment and any leading dimension
+ * are accepted; 16-byte aligned bases with leading dimensions and contiguous
+ * extents that are multiples of 8 elements take the vectorised path, the
+ * rest a slower predicated path with identical results.
+ *
+ * Ownership.  The caller allocates A, B and C in device memory (HBM) and
+ * keeps them alive until the stream work completes.  The library allocates
+ * no device memory, keeps no per-call state and never synchronises: each
+ * call only validates its arguments and enqueues one kernel on `stream`
+ * (a hipStream_t; NULL is the null stream).  C is fully overwritten
+ * (alpha = 1, beta = 0) and must not overlap A or B.
+ *
+ * Errors.  Argument errors are reported synchronously, before anything is
+ * enqueued, through the return value; tdg_last_error() then describes the
+ * cause (thread-local).  Faults inside a kernel surface at the caller's next
+ * synchronisation, as for any HIP kernel.
+ *   TDG_INVALID_VALUE  negative M, N, K or batch; a NULL pointer with work to
+ *                      do; a leading dimension or batch stride too small;
+ *                      an unknown dtype or a dtype combination not offered.
+ *   TDG_NOT_SUPPORTED  the current device is not gfx950.
+ *   TDG_LAUNCH_FAILED  the kernel launch was rejected by the HIP runtime.
+ * Degenerate sizes: M == 0, N == 0 or batch == 0 do nothing and succeed;
+ * K == 0 writes zeros to C (the empty sum).
+ */
+#ifndef TDG_H
+#define TDG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TDG_ABI_VERSION 1
+
+typedef enum { TDG_F16 = 0, TDG_BF16 = 1, TDG_F32 = 2 } tdg_dtype;
+
+typedef enum {
+    TDG_SUCCESS = 0,
+    TDG_INVALID_VALUE = 1,
+    TDG_NOT_SUPPORTED = 2,
+    TDG_LAUNCH_FAILED = 3
+} tdg_status;
+
+/* C (M x N) = A (M x K) * B (K x N).  ab_type in {TDG_F16, TDG_BF16} for both
+ * inputs; c_type in {TDG_F16, TDG_BF16, TDG_F32}. */
+tdg_status tdg_gemm_nn(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda,
+                       const void *B, int64_t ldb,
+                       void *C, int64_t ldc,
+                       tdg_dtype ab_type, tdg_dtype c_type, void *stream);
+
+/* C (M x N) = A (M x K) * B^T with B stored N x K (row stride ldb >= K). */
+tdg_status tdg_gemm_tn(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda,
+                       const void *B, int64_t ldb,
+                       void *C, int64_t ldc,
+                       tdg_dtype ab_type, tdg_dtype c_type, void *stream);
+
+/* `batch` independent NN products; problem z uses A + z*strideA,
+ * B + z*strideB, C + z*strideC (element offsets).  Each stride must be
+ * nonnegative, and strideC must keep the C matrices disjoint
+ * (strideC >= (M-1)*ldc + N when batch > 1). */
+tdg_status tdg_gemm_nn_batched(int64_t M, int64_t N, int64_t K,
+                               const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB,
+                               void *C, int64_t ldc, int64_t strideC,
+                               int64_t batch,
+                               tdg_dtype ab_type, tdg_dtype c_type, void *stream);
+
+/* `batch` independent TN products (B_z stored N x K). */
+tdg_status tdg_gemm_tn_batched(int64_t M, int64_t N, int64_t K,
+                               const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB,
+                               void *C, int64_t ldc, int64_t strideC,
+                               int64_t batch,
+                               tdg_dtype ab_type, tdg_dtype c_type, void *stream);
+
+/* Same as the batched calls, with the tile configuration forced: `config`
+ * is an index in [0, tdg_num_configs()) or -1 for the library's own choice.
+ * `transb` is 0 for NN and 1 for TN.  A forced configuration that cannot
+ * serve the arguments (the vectorised path on misaligned operands) returns
+ * TDG_INVALID_VALUE.  Meant for tests and tuning sweeps. */
+tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, int64_t strideA,
+                       const void *B, int64_t ldb, int64_t strideB,
+                       void *C, int64_t ldc, int64_t strideC,
+                       int64_t batch,
+                       tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream);
+
+/* Number of tile configurations and the name of configuration `config`
+ * (e.g. "256x256x64_w2x2_vec"); NULL for an index out of range. */
+int tdg_num_configs(void);
+const char *tdg_config_name(int config);
+
+/* The configuration the library would choose for these arguments (pointers
+ * are inspected for alignment only, never dereferenced); -1 on bad args. */
+int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda, const void *B, int64_t ldb,
+                      const void *C, int64_t ldc, int64_t batch,
+                      tdg_dtype ab_type, tdg_dtype c_type);
+
+const char *tdg_status_string(tdg_status status);
+/* Human-readable cause of this thread's most recent non-success ("" if none). */
+const char *tdg_last_error(void);
+int tdg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDG_H */

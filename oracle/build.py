@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+    cmd = ["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-pthread",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
            SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:

@@ -37,7 +37,7 @@
  *                     nominal and valid element ranges of the A tile, B tile
  *                     and output tile ([NT] s3, s4, s5).
  *
- * Build: gcc -O2 -fPIC -shared -pthread -ffp-contract=off (see build.py).
+ * Build: gcc -O3 -fPIC -shared -pthread -ffp-contract=off (see build.py).
  */
 #include <math.h>
 #include <pthread.h>
@@ -185,29 +185,33 @@ int orc_gemm(int transb, int fmt, int64_t M, int64_t N, int64_t K,
     if (nthreads < 1) nthreads = 1;
     if (nrows == 0 || N == 0 || batch == 0) return ORC_OK;
 
+    /* All 65536 bit patterns decoded once; element decoding is a lookup. */
+    double *lut = (double *)malloc(sizeof(double) * 65536);
+    if (!lut) return ORC_NO_MEM;
+    for (int v = 0; v < 65536; ++v) lut[v] = orc_decode(fmt, (uint16_t)v);
     double *Ad = (double *)malloc(sizeof(double) * (size_t)(nrows * (K ? K : 1)));
     double *Bd = (double *)malloc(sizeof(double) * (size_t)((K ? K : 1) * N));
     int64_t *all = NULL;
-    if (!Ad || !Bd) { free(Ad); free(Bd); return ORC_NO_MEM; }
+    if (!Ad || !Bd) { free(lut); free(Ad); free(Bd); return ORC_NO_MEM; }
     if (rows == NULL) {
         all = (int64_t *)malloc(sizeof(int64_t) * (size_t)M);
-        if (!all) { free(Ad); free(Bd); return ORC_NO_MEM; }
+        if (!all) { free(lut); free(Ad); free(Bd); return ORC_NO_MEM; }
         for (int64_t i = 0; i < M; ++i) all[i] = i;
         rows = all;
     }
     pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
     gemm_job *jobs = (gemm_job *)malloc(sizeof(gemm_job) * (size_t)nthreads);
-    if (!tid || !jobs) { free(Ad); free(Bd); free(all); free(tid); free(jobs); return ORC_NO_MEM; }
+    if (!tid || !jobs) { free(lut); free(Ad); free(Bd); free(all); free(tid); free(jobs); return ORC_NO_MEM; }
 
     for (int64_t b = 0; b < batch; ++b) {
         const uint16_t *Ab = A + b * sA;
         const uint16_t *Bb = B + b * sB;
         for (int64_t r = 0; r < nrows; ++r)
             for (int64_t p = 0; p < K; ++p)
-                Ad[r * K + p] = orc_decode(fmt, Ab[rows[r] * lda + p]);
+                Ad[r * K + p] = lut[Ab[rows[r] * lda + p]];
         for (int64_t p = 0; p < K; ++p)
             for (int64_t j = 0; j < N; ++j)
-                Bd[p * N + j] = orc_decode(fmt, Bb[b_index(transb, p, j, ldb)]);
+                Bd[p * N + j] = lut[Bb[b_index(transb, p, j, ldb)]];
         int nt = nthreads;
         if (nt > nrows) nt = (int)nrows;
         for (int t = 0; t < nt; ++t) {
@@ -228,7 +232,7 @@ int orc_gemm(int transb, int fmt, int64_t M, int64_t N, int64_t K,
         for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
         for (int t = started + 1; t < nt; ++t) gemm_worker(&jobs[t]);  /* spawn failure: run inline */
     }
-    free(Ad); free(Bd); free(all); free(tid); free(jobs);
+    free(lut); free(Ad); free(Bd); free(all); free(tid); free(jobs);
     return ORC_OK;
 }
 

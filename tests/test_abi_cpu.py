@@ -1,0 +1,130 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+declared in include/tdg.h, and rejects bad arguments synchronously, before
+touching any device (no compute call is made here)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tdg.h")
+LIB = os.path.join(ROOT, "tiled_dense_gemm_03_amd", "libtdg.so")
+
+
+@pytest.fixture(scope="module")
+def tdg():
+    if not os.path.exists(LIB):
+        from tiled_dense_gemm_03_amd import build
+        build.build()
+    import tiled_dense_gemm_03_amd as t
+    return t
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tdg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("tdg_gemm_nn", "tdg_gemm_tn", "tdg_gemm_nn_batched", "tdg_gemm_tn_batched",
+                     "tdg_status_string", "tdg_last_error", "tdg_abi_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(tdg):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(tdg._binding.lib, name)
+    assert set(tdg.EXPORTED) == set(declared_functions())
+
+
+def test_version_configs_and_status_strings(tdg):
+    assert tdg.tdg_abi_version() == 1
+    n = tdg.tdg_num_configs()
+    assert n >= 2
+    names = [tdg.tdg_config_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert tdg.tdg_config_name(n) is None and tdg.tdg_config_name(-1) is None
+    assert tdg.tdg_status_string(tdg.TDG_SUCCESS) == "TDG_SUCCESS"
+    assert tdg.tdg_status_string(tdg.TDG_INVALID_VALUE) == "TDG_INVALID_VALUE"
+    assert tdg.tdg_status_string(99) == "TDG_UNKNOWN_STATUS"
+
+
+P = 1 << 20  # a fake, 16-byte aligned address: never dereferenced by these calls
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((-1, 8, 8, P, 8, P, 8, P, 8, 0, 0), "negative"),
+    ((8, -1, 8, P, 8, P, 8, P, 8, 0, 0), "negative"),
+    ((8, 8, -1, P, 8, P, 8, P, 8, 0, 0), "negative"),
+    ((8, 8, 16, P, 8, P, 8, P, 8, 0, 0), "lda"),
+    ((8, 16, 8, P, 8, P, 8, P, 16, 0, 0), "ldb"),
+    ((8, 16, 8, P, 8, P, 16, P, 8, 0, 0), "ldc"),
+    ((8, 8, 8, P, 8, P, 8, P, 8, 2, 0), "ab_type"),
+    ((8, 8, 8, P, 8, P, 8, P, 8, 0, 5), "c_type"),
+    ((8, 8, 8, None, 8, P, 8, P, 8, 0, 0), "NULL"),
+    ((8, 8, 8, P, 8, P, 8, None, 8, 0, 0), "NULL"),
+    ((8, 8, 8, P + 1, 8, P, 8, P, 8, 0, 0), "aligned"),
+    ((8, 8, 8, P, 8, P, 8, P + 2, 8, 0, 2), "aligned"),
+    ((1 << 31, 8, 8, P, 8, P, 8, P, 8, 0, 0), "2^31"),
+])
+def test_invalid_arguments_rejected_before_launch(tdg, args, needle):
+    st = tdg.tdg_gemm_nn(*args, None)
+    assert st == tdg.TDG_INVALID_VALUE
+    assert needle in tdg.tdg_last_error()
+
+
+def test_tn_leading_dimension_rule(tdg):
+    # TN: B is N x K, so ldb must be >= K (not N)
+    assert tdg.tdg_gemm_tn(8, 32, 16, P, 16, P, 8, P, 32, 0, 0, None) == tdg.TDG_INVALID_VALUE
+    assert "ldb" in tdg.tdg_last_error()
+
+
+def test_batched_rules(tdg):
+    # negative batch, negative stride, overlapping C
+    assert tdg.tdg_gemm_nn_batched(8, 8, 8, P, 8, 64, P, 8, 64, P, 8, 64, -1, 0, 0, None) == tdg.TDG_INVALID_VALUE
+    assert tdg.tdg_gemm_nn_batched(8, 8, 8, P, 8, -64, P, 8, 64, P, 8, 64, 2, 0, 0, None) == tdg.TDG_INVALID_VALUE
+    assert tdg.tdg_gemm_tn_batched(8, 8, 8, P, 8, 64, P, 8, 64, P, 8, 32, 2, 0, 0, None) == tdg.TDG_INVALID_VALUE
+    assert "overlap" in tdg.tdg_last_error()
+
+
+def test_empty_problems_succeed_without_a_device(tdg):
+    assert tdg.tdg_gemm_nn(0, 8, 8, None, 8, None, 8, None, 8, 0, 0, None) == tdg.TDG_SUCCESS
+    assert tdg.tdg_gemm_tn(8, 0, 8, None, 8, None, 8, None, 1, 1, 2, None) == tdg.TDG_SUCCESS
+    assert tdg.tdg_gemm_nn_batched(8, 8, 8, None, 8, 0, None, 8, 0, None, 8, 0, 0, 0, 0, None) == tdg.TDG_SUCCESS
+
+
+def test_forced_config_checks(tdg):
+    n = tdg.tdg_num_configs()
+    assert tdg.tdg_gemm_ex(0, 8, 8, 8, P, 8, 0, P, 8, 0, P, 8, 0, 1, 0, 0, n, None) == tdg.TDG_INVALID_VALUE
+    vec0 = [i for i in range(n) if tdg.tdg_config_name(i).endswith("_vec")][0]
+    # misaligned A (odd address) cannot take a vectorised configuration
+    assert tdg.tdg_gemm_ex(0, 8, 8, 8, P + 2, 8, 0, P, 8, 0, P, 8, 0, 1, 0, 0, vec0, None) == tdg.TDG_INVALID_VALUE
+    assert "aligned" in tdg.tdg_last_error()
+
+
+def test_config_selection(tdg):
+    def sel(transb, M, N, K, a=P, lda=None, b=P, ldb=None, batch=1):
+        lda = lda or K
+        ldb = ldb or (K if transb else N)
+        return tdg.tdg_config_name(tdg.tdg_select_config(transb, M, N, K, a, lda, b, ldb, P, N, batch, 0, 0))
+    assert sel(0, 8192, 8192, 8192).endswith("_vec")
+    assert sel(0, 4095, 5000, 3000).endswith("_vec")
+    assert sel(0, 65, 97, 130).endswith("_pred")            # K not a multiple of 8
+    assert sel(1, 64, 97, 128).endswith("_vec")             # TN: N may be ragged
+    assert sel(0, 64, 97, 128).endswith("_pred")            # NN: B rows need N % 8 == 0
+    assert sel(0, 64, 64, 64, a=P + 2).endswith("_pred")    # misaligned base
+    assert tdg.tdg_select_config(0, -1, 8, 8, P, 8, P, 8, P, 8, 1, 0, 0) == -1
+
+
+def test_no_device_is_reported_not_run(tdg):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = tdg.tdg_gemm_nn(64, 64, 64, P, 64, P, 64, P, 64, 0, 0, None)
+    assert st == tdg.TDG_NOT_SUPPORTED

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Covers the six workloads of the method's test plan at full size (row-sampled
+where the oracle cannot do the whole product in seconds), their integer
+variants bit for bit, every tile configuration on ragged shapes, strided
+operands, guard bands and NaN poison in padding, degenerate sizes and
+run-to-run determinism.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from parity import OUT_TORCH, check_exact, check_tol, ref_gemm, to_f64
+from workloads import WORKLOADS, bits, make_inputs, sample_rows, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tdg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_gemm_03_amd as t
+    return t
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_gemm(tdg, a, b, layout, out_dtype, config=-1):
+    ad, bd = a.cuda(), b.cuda()
+    c = tdg.gemm(ad, bd, layout=layout, out_dtype=OUT_TORCH[out_dtype], config=config)
+    torch.cuda.synchronize()
+    return c.cpu()
+
+
+# ---------------------------------------------------------------------------
+# The six workloads at full size
+# ---------------------------------------------------------------------------
+
+SMALL = ["worked_128x256x192", "tn_exact_1024"]
+LARGE = ["nn_f16_4096", "nn_bf16_8192", "nn_f16_ragged_4095x5000x3000", "tn_f16_batched_32x2048x2048x128"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workloads_whole(tdg, name):
+    w = WORKLOADS[name]
+    announce(name)
+    a, b = workload_inputs(w)
+    c = gpu_gemm(tdg, a, b, w.layout, w.out_dtype)
+    ref = ref_gemm(a, b, w.in_dtype, w.layout)
+    if w.exact:
+        check_exact(c, ref, w.out_dtype, name)
+    else:
+        check_tol(c, ref, w.out_dtype, w.K, name)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workloads_sampled_rows(tdg, name):
+    """Full-size product in the launch configuration the benchmark times;
+    the oracle computes the first and last row of every 256-row band plus 64
+    seeded rows (every tile row and tile column is touched)."""
+    w = WORKLOADS[name]
+    announce(name)
+    a, b = workload_inputs(w)
+    c = gpu_gemm(tdg, a, b, w.layout, w.out_dtype)
+    rows = sample_rows(w.M)
+    if w.batch:
+        # every problem of the batch, sampled rows of each
+        ref = ref_gemm(a, b, w.in_dtype, w.layout, rows=rows)
+        check_tol(c[:, rows], ref, w.out_dtype, w.K, name)
+    else:
+        ref = ref_gemm(a, b, w.in_dtype, w.layout, rows=rows)
+        check_tol(c[rows], ref, w.out_dtype, w.K, name)
+
+
+@pytest.mark.parametrize("name", ["worked_128x256x192", "nn_f16_4096", "nn_bf16_8192",
+                                  "nn_f16_ragged_4095x5000x3000", "tn_f16_batched_32x2048x2048x128"])
+def test_integer_variants_bit_exact(tdg, name):
+    """The same shapes, layouts and dtypes with integer inputs in {-2..2}:
+    the GPU result must equal the oracle's exact sum, rounded once."""
+    w = WORKLOADS[name]
+    announce(name, "ints")
+    a, b = make_inputs(w.M, w.N, w.K, w.layout, w.in_dtype, "ints", seed=w.seed + 1000, batch=w.batch)
+    c = gpu_gemm(tdg, a, b, w.layout, w.out_dtype)
+    if w.M * w.N * w.K * max(1, w.batch) <= 2 ** 28:
+        check_exact(c, ref_gemm(a, b, w.in_dtype, w.layout), w.out_dtype, name)
+        return
+    rows = sample_rows(w.M)
+    ref = ref_gemm(a, b, w.in_dtype, w.layout, rows=rows)
+    check_exact(c[:, rows] if w.batch else c[rows], ref, w.out_dtype, name)
+
+
+# ---------------------------------------------------------------------------
+# Every tile configuration on ragged shapes
+# ---------------------------------------------------------------------------
+
+# (M, N, K): tails in M, N and K; "several full K tiles then a tail"; one tile;
+# fewer rows or columns than one MFMA tile.  K and N are multiples of 8 so the
+# vectorised configurations apply; the predicated ones also get odd sizes.
+VEC_SHAPES = [(1, 8, 8), (17, 24, 16), (33, 40, 72), (64, 64, 64), (65, 72, 200), (127, 136, 256),
+              (129, 264, 136), (255, 248, 520), (257, 520, 64), (300, 8, 1032)]
+PRED_SHAPES = [(1, 1, 1), (2, 3, 5), (15, 17, 31), (33, 31, 63), (65, 97, 130), (63, 129, 197),
+               (130, 65, 257), (257, 255, 129)]
+
+
+def _config_ids(tdg, vec):
+    return [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i).endswith("_vec" if vec else "_pred")]
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+def test_every_config_integer_exact(tdg, layout, in_dtype, out_dtype):
+    for vec, shapes in ((True, VEC_SHAPES), (False, VEC_SHAPES + PRED_SHAPES)):
+        for cfg in _config_ids(tdg, vec):
+            for (M, N, K) in shapes:
+                announce(layout, in_dtype, out_dtype, tdg.tdg_config_name(cfg), M, N, K)
+                a, b = make_inputs(M, N, K, layout, in_dtype, "ints", seed=M * 7 + N * 3 + K)
+                c = gpu_gemm(tdg, a, b, layout, out_dtype, config=cfg)
+                check_exact(c, ref_gemm(a, b, in_dtype, layout), out_dtype,
+                            "%s %s %dx%dx%d" % (layout, tdg.tdg_config_name(cfg), M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_every_config_random_tolerance(tdg, layout):
+    for cfg in range(tdg.tdg_num_configs()):
+        vec = tdg.tdg_config_name(cfg).endswith("_vec")
+        for (M, N, K) in ([(65, 72, 200), (257, 264, 520)] + ([] if vec else [(63, 129, 197)])):
+            for in_dtype, out_dtype in (("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")):
+                announce(layout, tdg.tdg_config_name(cfg), M, N, K, in_dtype, out_dtype)
+                a, b = make_inputs(M, N, K, layout, in_dtype, "uniform", seed=cfg + 17)
+                c = gpu_gemm(tdg, a, b, layout, out_dtype, config=cfg)
+                check_tol(c, ref_gemm(a, b, in_dtype, layout), out_dtype, K, "cfg %d" % cfg)
+
+
+# ---------------------------------------------------------------------------
+# Strides, guard bands, NaN poison
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("pad", [8, 3])
+def test_strided_operands_guard_band_and_nan_padding(tdg, layout, pad):
+    """Operands are views into larger buffers whose padding columns hold NaN;
+    C is a view into a buffer pre-filled with a sentinel.  The NaN must not
+    reach C and nothing outside C's view may change.  pad=3 breaks 16-byte
+    alignment of the rows (predicated path), pad=8 keeps it (vector path)."""
+    M, N, K = 131, 136, 200
+    announce("strided", layout, pad)
+    a, b = make_inputs(M, N, K, layout, "f16", "ints", seed=77)
+    A = torch.full((M, K + pad), float("nan"), dtype=torch.float16)
+    A[:, :K] = a
+    rb, cb = b.shape
+    B = torch.full((rb, cb + pad), float("nan"), dtype=torch.float16)
+    B[:, :cb] = b
+    Cbuf = torch.full((M + 2, N + 2 * pad), -12345.0, dtype=torch.float32).cuda()
+    Cview = Cbuf[1:M + 1, pad:pad + N]
+    tdg.gemm(A.cuda()[:, :K], B.cuda()[:, :cb], layout=layout, out_dtype=torch.float32, out=Cview)
+    torch.cuda.synchronize()
+    host = Cbuf.cpu()
+    check_exact(host[1:M + 1, pad:pad + N], ref_gemm(a, b, "f16", layout), "f32", "strided")
+    mask = torch.ones_like(host, dtype=torch.bool)
+    mask[1:M + 1, pad:pad + N] = False
+    assert torch.all(host[mask] == -12345.0), "write outside C"
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_batched_strided(tdg, layout):
+    batch, M, N, K = 5, 70, 88, 136
+    announce("batched", layout)
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=5, batch=batch)
+    c = gpu_gemm(tdg, a, b, layout, "f32")
+    ref = ref_gemm(a, b, "bf16", layout)
+    check_exact(c, ref, "f32", "batched")
+    # broadcast B (2-D b with batched a)
+    c2 = tdg.gemm(a.cuda(), b[0].cuda(), layout=layout, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref2 = ref_gemm(a, b[0:1].expand(batch, *b.shape[1:]).contiguous(), "bf16", layout)
+    check_exact(c2.cpu(), ref2, "f32", "broadcast B")
+
+
+# ---------------------------------------------------------------------------
+# Degenerate sizes, pinned page examples, determinism, subnormals
+# ---------------------------------------------------------------------------
+
+def test_k_zero_writes_zeros_and_empty_is_noop(tdg):
+    announce("degenerate")
+    a = torch.empty((33, 0), dtype=torch.float16, device="cuda")
+    b = torch.empty((0, 40), dtype=torch.float16, device="cuda")
+    out = torch.full((33, 40), 7.0, dtype=torch.float32, device="cuda")
+    tdg.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    a = torch.empty((0, 16), dtype=torch.float16, device="cuda")
+    b = torch.ones((16, 8), dtype=torch.float16, device="cuda")
+    assert tdg.gemm(a, b).shape == (0, 8)
+
+
+def test_page_examples_on_gpu(tdg, golden):
+    """All-ones over the 65 x 97 x 130 tail case gives 130 everywhere, and
+    2048 + 1 + 1 gives 2050 with the fp32 accumulator and fp16 output
+    (NineToothed GEMM primer, s6 and s8 exercise 3)."""
+    announce("page examples")
+    o = golden["all_ones"]
+    a = torch.ones((o["M"], o["K"]), dtype=torch.float16)
+    b = torch.ones((o["K"], o["N"]), dtype=torch.float16)
+    for cfg in range(tdg.tdg_num_configs()):
+        if tdg.tdg_config_name(cfg).endswith("_vec"):
+            continue   # K = 130 is not a whole number of 8-element granules
+        c = gpu_gemm(tdg, a, b, "nn", "f16", config=cfg)
+        assert torch.all(c == o["value"])
+    c = gpu_gemm(tdg, a, b, "nn", "f16")
+    assert c.shape == (o["M"], o["N"]) and torch.all(c == o["value"])
+    e = golden["fp32_accumulation"]
+    a = torch.tensor([e["terms"]], dtype=torch.float16)
+    b = torch.ones((3, 1), dtype=torch.float16)
+    c = gpu_gemm(tdg, a, b, "nn", "f16")
+    assert float(c[0, 0]) == e["final_fp16_output_from_fp32_accumulator"]
+
+
+@pytest.mark.parametrize("name", ["nn_f16_4096", "tn_f16_batched_32x2048x2048x128"])
+def test_determinism(tdg, name):
+    w = WORKLOADS[name]
+    announce("determinism", name)
+    a, b = workload_inputs(w)
+    ad, bd = a.cuda(), b.cuda()
+    c1 = tdg.gemm(ad, bd, layout=w.layout, out_dtype=OUT_TORCH[w.out_dtype])
+    c2 = tdg.gemm(ad, bd, layout=w.layout, out_dtype=OUT_TORCH[w.out_dtype])
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.uint8) if c1.dtype != torch.float32 else c1.view(torch.int32),
+                       c2.view(torch.uint8) if c2.dtype != torch.float32 else c2.view(torch.int32))
+
+
+def test_fp16_subnormal_inputs(tdg):
+    """Subnormal fp16 inputs are used as their exact values (no flush): with
+    A = 2^-24 * small integers and B = small integers the exact products are
+    multiples of 2^-24, and the fp32 output holds them exactly."""
+    announce("subnormals")
+    M, N, K = 64, 72, 136
+    gen = torch.Generator().manual_seed(3)
+    ai = torch.randint(-3, 4, (M, K), generator=gen).to(torch.float64)
+    bi = torch.randint(-3, 4, (K, N), generator=gen).to(torch.float64)
+    a = (ai * 2.0 ** -24).to(torch.float16)          # subnormal fp16 values
+    b = bi.to(torch.float16)
+    assert torch.equal(a.to(torch.float64), ai * 2.0 ** -24)
+    c = gpu_gemm(tdg, a, b, "nn", "f32")
+    ref = ref_gemm(a, b, "f16", "nn")
+    check_exact(c, ref, "f32", "subnormal")

@@ -1,0 +1,106 @@
+"""Tensor-level front of the C ABI: shape/stride marshalling only.
+
+Accepts row-major torch tensors (unit last stride, any row stride) on a ROCm
+device, reads their sizes, strides and data pointers, and makes exactly one
+call into ``libtdg.so`` on ``torch.cuda.current_stream()``.  No arithmetic of
+the product happens here.
+"""
+import torch
+
+from . import _binding as _b
+
+_AB = {torch.float16: _b.TDG_F16, torch.bfloat16: _b.TDG_BF16}
+_CT = {torch.float16: _b.TDG_F16, torch.bfloat16: _b.TDG_BF16, torch.float32: _b.TDG_F32}
+
+
+class TdgError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("%s: %s" % (_b.tdg_status_string(status), detail))
+        self.status = status
+
+
+def _check(status):
+    if status != _b.TDG_SUCCESS:
+        raise TdgError(status, _b.tdg_last_error())
+
+
+def _row_major(t, name):
+    if t.dim() not in (2, 3):
+        raise ValueError("%s must be 2-D or 3-D (batched), got %d-D" % (name, t.dim()))
+    if t.size(-1) > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must have unit stride in its last dimension" % name)
+    return t
+
+
+def config_names():
+    return [_b.tdg_config_name(i) for i in range(_b.tdg_num_configs())]
+
+
+def _dims(a, b, layout):
+    M, K = a.shape[-2], a.shape[-1]
+    if layout == "nn":
+        Kb, N = b.shape[-2], b.shape[-1]
+    elif layout == "tn":
+        N, Kb = b.shape[-2], b.shape[-1]
+    else:
+        raise ValueError("layout must be 'nn' or 'tn'")
+    if Kb != K:
+        raise ValueError("inner dimensions differ: A has K=%d, B has K=%d" % (K, Kb))
+    return M, N, K
+
+
+def _ld(t):
+    # row stride in elements; a single-row matrix may report any stride
+    return max(t.stride(-2), t.size(-1), 1)
+
+
+def select_config(a, b, layout="nn", out_dtype=None):
+    """Index of the tile configuration the library picks for these operands."""
+    M, N, K = _dims(a, b, layout)
+    batch = a.shape[0] if a.dim() == 3 else 1
+    ct = _CT[out_dtype or a.dtype]
+    return _b.tdg_select_config(1 if layout == "tn" else 0, M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
+                                None, N, batch, _AB[a.dtype], ct)
+
+
+def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1):
+    """C = A @ B (layout "nn", b is (K, N)) or A @ B^T ("tn", b is (N, K)).
+
+    a: (M, K) or (batch, M, K); b likewise batched or not (a 2-D b is shared
+    by every problem of a batched a).  fp16/bf16 inputs of the same dtype,
+    fp32 accumulation; out_dtype defaults to the input dtype and may be
+    float32.  ``out`` (row-major, unit last stride) is written in place;
+    otherwise a new contiguous tensor is returned.  ``config`` forces a tile
+    configuration (tests and sweeps); -1 lets the library choose.
+    """
+    _row_major(a, "a")
+    _row_major(b, "b")
+    if a.dtype not in _AB or b.dtype != a.dtype:
+        raise TypeError("a and b must both be float16 or both bfloat16 (got %s, %s)" % (a.dtype, b.dtype))
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("a and b must be device tensors")
+    M, N, K = _dims(a, b, layout)
+    batched = a.dim() == 3 or b.dim() == 3
+    batch = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError("batch sizes differ")
+    odt = out_dtype or (out.dtype if out is not None else a.dtype)
+    if odt not in _CT:
+        raise TypeError("out_dtype must be float16, bfloat16 or float32")
+    shape = (batch, M, N) if batched else (M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=odt, device=a.device)
+    else:
+        if tuple(out.shape) != shape or out.dtype != odt:
+            raise ValueError("out must be %s of %s, got %s of %s" % (shape, odt, tuple(out.shape), out.dtype))
+        _row_major(out, "out")
+    sA = a.stride(0) if a.dim() == 3 else 0
+    sB = b.stride(0) if b.dim() == 3 else 0
+    sC = out.stride(0) if out.dim() == 3 else 0
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    with torch.cuda.device(a.device):
+        _check(_b.tdg_gemm_ex(1 if layout == "tn" else 0, M, N, K,
+                              a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
+                              out.data_ptr(), _ld(out), sC, batch,
+                              _AB[a.dtype], _CT[odt], int(config), stream))
+    return out

@@ -1,0 +1,49 @@
+// gemm_inst.hip -- instantiates the GEMM kernel for one (layout, input type)
+// pair; compiled once per pair with -DTDG_TRANSB=0|1 -DTDG_AB=0|1 so the
+// instantiations build in parallel.  Exposes one launcher per pair.
+#include "gemm_kernel.hpp"
+
+#ifndef TDG_TRANSB
+#error "TDG_TRANSB must be defined"
+#endif
+#ifndef TDG_AB
+#error "TDG_AB must be defined"
+#endif
+
+namespace tdg {
+
+template <int BM, int BN, int WM, int WN, bool VEC>
+static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
+    constexpr bool TB = TDG_TRANSB != 0;
+    switch (ct) {
+    case OUT_F16:
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_F16, VEC>), dim3((unsigned)grid),
+                           dim3(NTHREADS), 0, s, a);
+        break;
+    case OUT_BF16:
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_BF16, VEC>), dim3((unsigned)grid),
+                           dim3(NTHREADS), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_F32, VEC>), dim3((unsigned)grid),
+                           dim3(NTHREADS), 0, s, a);
+        break;
+    }
+    return hipGetLastError();
+}
+
+#define TDG_CAT2(a, b) a##b
+#define TDG_CAT(a, b) TDG_CAT2(a, b)
+#define TDG_LAUNCHER TDG_CAT(TDG_CAT(launch_t, TDG_TRANSB), TDG_CAT(_ab, TDG_AB))
+
+hipError_t TDG_LAUNCHER(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
+    switch (cfg) {
+#define TDG_CASE(ID, BM, BN, WM, WN, VEC, NAME) \
+    case ID: return launch_ct<BM, BN, WM, WN, VEC>(ct, a, grid, s);
+        TDG_CONFIG_LIST(TDG_CASE)
+#undef TDG_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tdg
