@@ -79,8 +79,10 @@ def time_workload(tdg, torch, w, steps, warmup):
     return wall * 1e3 / steps, kernel_ms, tdg.tdg_config_name(cfg)
 
 
-def cpu_baseline(w, seconds_target=15.0):
-    """The oracle, unchanged, on a bounded row sample of the same workload."""
+def cpu_baseline(w, seconds_min=10.0):
+    """The oracle, unchanged, on a bounded row sample of the same workload:
+    evenly spaced output rows (all columns, full K), doubling the row count
+    until one run takes at least ``seconds_min`` (or covers every row)."""
     import numpy as np
     from oracle import oracle
     from workloads import bits, workload_inputs
@@ -90,21 +92,32 @@ def cpu_baseline(w, seconds_target=15.0):
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit():
         nt = min(nt, int(omp))
-    # calibrate on a few rows, then size the sample to ~seconds_target
-    probe = np.arange(0, w.M, max(1, w.M // 8), dtype=np.int64)[:8]
-    t0 = time.perf_counter()
-    oracle.gemm(ab, bb, w.in_dtype, w.layout, rows=probe, nthreads=nt)
-    t_probe = time.perf_counter() - t0
-    per_row = t_probe / len(probe)
-    nrows = int(max(8, min(w.M, seconds_target / max(per_row, 1e-9))))
-    rows = np.linspace(0, w.M - 1, nrows).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.gemm(ab, bb, w.in_dtype, w.layout, rows=rows, nthreads=nt)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * w.N * w.K
+    nrows = 16
+    while True:
+        rows = np.linspace(0, w.M - 1, min(nrows, w.M)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm(ab, bb, w.in_dtype, w.layout, rows=rows, nthreads=nt)
+        dt = time.perf_counter() - t0
+        if dt >= seconds_min or nrows >= w.M:
+            break
+        nrows *= 2
+    flops = 2.0 * len(rows) * w.N * w.K * max(1, w.batch)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
-            "sample": "%d of %d output rows (all %d columns, full K=%d), %.1f s; value = 2*rows*N*K / time"
-                      % (len(rows), w.M, w.N, w.K, dt)}
+            "sample": "%d of %d output rows%s (all %d columns, full K=%d), %.1f s; value = 2*rows*N*K%s / time"
+                      % (len(rows), w.M, " of each of %d problems" % w.batch if w.batch else "", w.N, w.K, dt,
+                         "*batch" if w.batch else "")}
+
+
+def calibrate_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain copy kernel of known size, for scaling the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE): each dispatch of the elementwise multiply-by-one
+    reads nbytes and writes nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "dispatches": reps}), flush=True)
 
 
 def main():
@@ -115,6 +128,8 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; --gpus %d is not offered (the product shards "
@@ -128,6 +143,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     w = WORKLOADS[args.workload]
     ms, kernel_ms, cfg_name = time_workload(tdg, torch, w, args.steps, args.warmup)
     flops = w.flops

@@ -110,7 +110,8 @@ PRED_SHAPES = [(1, 1, 1), (2, 3, 5), (15, 17, 31), (33, 31, 63), (65, 97, 130), 
 
 
 def _config_ids(tdg, vec):
-    return [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i).endswith("_vec" if vec else "_pred")]
+    """Vectorised configurations (aligned operands only) or the predicated ones."""
+    return [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i).endswith("_pred") != vec]
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn"])
@@ -129,7 +130,7 @@ def test_every_config_integer_exact(tdg, layout, in_dtype, out_dtype):
 @pytest.mark.parametrize("layout", ["nn", "tn"])
 def test_every_config_random_tolerance(tdg, layout):
     for cfg in range(tdg.tdg_num_configs()):
-        vec = tdg.tdg_config_name(cfg).endswith("_vec")
+        vec = not tdg.tdg_config_name(cfg).endswith("_pred")
         for (M, N, K) in ([(65, 72, 200), (257, 264, 520)] + ([] if vec else [(63, 129, 197)])):
             for in_dtype, out_dtype in (("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")):
                 announce(layout, tdg.tdg_config_name(cfg), M, N, K, in_dtype, out_dtype)
@@ -209,7 +210,7 @@ def test_page_examples_on_gpu(tdg, golden):
     a = torch.ones((o["M"], o["K"]), dtype=torch.float16)
     b = torch.ones((o["K"], o["N"]), dtype=torch.float16)
     for cfg in range(tdg.tdg_num_configs()):
-        if tdg.tdg_config_name(cfg).endswith("_vec"):
+        if not tdg.tdg_config_name(cfg).endswith("_pred"):
             continue   # K = 130 is not a whole number of 8-element granules
         c = gpu_gemm(tdg, a, b, "nn", "f16", config=cfg)
         assert torch.all(c == o["value"])

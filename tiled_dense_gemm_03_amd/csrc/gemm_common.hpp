@@ -19,14 +19,21 @@ struct GemmArgs {
 
 }  // namespace tdg
 
-// X(id, BM, BN, WM, WN, VEC, name): BM x BN workgroup tile (BK = 64),
-// WM x WN waves, VEC = vectorised loads (aligned operands) or the
-// predicated element-load path.
-#define TDG_CONFIG_LIST(X)                                   \
-    X(0, 256, 256, 2, 2, true, "256x256x64_w2x2_vec")        \
-    X(1, 256, 128, 2, 2, true, "256x128x64_w2x2_vec")        \
-    X(2, 128, 256, 2, 2, true, "128x256x64_w2x2_vec")        \
-    X(3, 128, 128, 2, 2, true, "128x128x64_w2x2_vec")        \
-    X(4, 64, 64, 2, 2, true, "64x64x64_w2x2_vec")            \
-    X(5, 64, 64, 2, 2, false, "64x64x64_w2x2_pred")          \
-    X(6, 128, 128, 2, 2, false, "128x128x64_w2x2_pred")
+// X(id, KIND, BM, BN, BK, ST, WM, WN, VEC, name): ids run 0, 1, 2, ... in
+// list order (checked at compile time).  BM x BN workgroup tile, WM x WN
+// waves.  KIND 1 = the direct-to-LDS kernel (aligned operands only) with K
+// tiles of BK and ST pipeline stages; KIND 0 = the register-staged kernel
+// (BK 64, two stages), VEC = vectorised loads (aligned operands) or the
+// predicated element-load path (any operands).
+#define TDG_CONFIG_LIST(X)                                                   \
+    X(0, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
+    X(1, 1, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_lds")           \
+    X(2, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
+    X(3, 1, 256, 256, 32, 4, 2, 2, true, "256x256x32_s4_w2x2_lds")           \
+    X(4, 1, 256, 128, 64, 3, 2, 2, true, "256x128x64_s3_w2x2_lds")           \
+    X(5, 1, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_lds")           \
+    X(6, 1, 128, 128, 32, 4, 2, 2, true, "128x128x32_s4_w2x2_lds")           \
+    X(7, 0, 128, 128, 64, 2, 2, 2, true, "128x128x64_w2x2_vec")              \
+    X(8, 0, 64, 64, 64, 2, 2, 2, true, "64x64x64_w2x2_vec")                  \
+    X(9, 0, 64, 64, 64, 2, 2, 2, false, "64x64x64_w2x2_pred")                \
+    X(10, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")

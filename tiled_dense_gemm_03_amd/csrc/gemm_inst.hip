@@ -1,6 +1,7 @@
 // gemm_inst.hip -- instantiates the GEMM kernel for one (layout, input type)
 // pair; compiled once per pair with -DTDG_TRANSB=0|1 -DTDG_AB=0|1 so the
 // instantiations build in parallel.  Exposes one launcher per pair.
+#include "gemm_fast.hpp"
 #include "gemm_kernel.hpp"
 
 #ifndef TDG_TRANSB
@@ -12,24 +13,30 @@
 
 namespace tdg {
 
-template <int BM, int BN, int WM, int WN, bool VEC>
+template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TB, int CT, bool VEC>
+static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
+    if constexpr (KIND == 1) {
+        hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WM, WN, BK, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
+                           dim3(WM * WN * 64), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, CT, VEC>), dim3((unsigned)grid),
+                           dim3(NTHREADS), 0, s, a);
+    }
+}
+
+template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool VEC>
 static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     constexpr bool TB = TDG_TRANSB != 0;
-    switch (ct) {
-    case OUT_F16:
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_F16, VEC>), dim3((unsigned)grid),
-                           dim3(NTHREADS), 0, s, a);
-        break;
-    case OUT_BF16:
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_BF16, VEC>), dim3((unsigned)grid),
-                           dim3(NTHREADS), 0, s, a);
-        break;
-    default:
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, OUT_F32, VEC>), dim3((unsigned)grid),
-                           dim3(NTHREADS), 0, s, a);
-        break;
+    if constexpr (KIND == 1 && !TB && BN / 8 < 16) {
+        return hipErrorInvalidValue;   // NN direct-to-LDS kernel needs BN >= 128
+    } else {
+        switch (ct) {
+        case OUT_F16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_F16, VEC>(a, grid, s); break;
+        case OUT_BF16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_BF16, VEC>(a, grid, s); break;
+        default: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_F32, VEC>(a, grid, s); break;
+        }
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 #define TDG_CAT2(a, b) a##b
@@ -38,8 +45,8 @@ static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t
 
 hipError_t TDG_LAUNCHER(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     switch (cfg) {
-#define TDG_CASE(ID, BM, BN, WM, WN, VEC, NAME) \
-    case ID: return launch_ct<BM, BN, WM, WN, VEC>(ct, a, grid, s);
+#define TDG_CASE(ID, KIND, BM, BN, BK, ST, WM, WN, VEC, NAME) \
+    case ID: return launch_ct<KIND, BM, BN, BK, ST, WM, WN, VEC>(ct, a, grid, s);
         TDG_CONFIG_LIST(TDG_CASE)
 #undef TDG_CASE
     default: return hipErrorInvalidValue;

@@ -27,17 +27,25 @@ hipError_t launch_t1_ab1(int cfg, int ct, const GemmArgs &a, int64_t grid, hipSt
 namespace {
 
 struct Config {
-    int bm, bn, wm, wn;
+    int kind, bm, bn, bk, stages, wm, wn;
     bool vec;
     const char *name;
 };
 
 const Config kConfigs[] = {
-#define TDG_ROW(ID, BM, BN, WM, WN, VEC, NAME) {BM, BN, WM, WN, VEC, NAME},
+#define TDG_ROW(ID, KIND, BM, BN, BK, ST, WM, WN, VEC, NAME) {KIND, BM, BN, BK, ST, WM, WN, VEC, NAME},
     TDG_CONFIG_LIST(TDG_ROW)
 #undef TDG_ROW
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+
+constexpr int kConfigIds[] = {
+#define TDG_ID(ID, KIND, BM, BN, BK, ST, WM, WN, VEC, NAME) ID,
+    TDG_CONFIG_LIST(TDG_ID)
+#undef TDG_ID
+};
+constexpr bool ids_in_order(int i) { return i == kNumConfigs || (kConfigIds[i] == i && ids_in_order(i + 1)); }
+static_assert(ids_in_order(0), "configuration ids must be 0, 1, 2, ... in list order");
 
 thread_local char g_err[512] = "";
 
@@ -88,14 +96,46 @@ bool vec_ok(int transb, int64_t N, int64_t K, const void *A, int64_t lda, int64_
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int choose(bool vec, int64_t M, int64_t N, int64_t batch) {
-    if (!vec) {
-        return (cdiv(M, 128) * cdiv(N, 128) * batch >= 256) ? 6 : 5;
-    }
+// Whether configuration `cf` can serve the operands: the vectorised kinds
+// need vec_ok; the direct-to-LDS kind also needs every in-tile byte offset
+// below 2^31 (buffer offsets are 32-bit) and, for NN, B rows of at least 16
+// granules in LDS.
+bool config_ok(const Config &cf, int transb, bool vec, int64_t lda, int64_t ldb, int64_t ldc, int c_type) {
+    if (!cf.vec) return true;
+    if (!vec) return false;
+    if (cf.kind < 1) return true;
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t es = (c_type == TDG_F32) ? 4 : 2;
+    if ((int64_t)cf.bm * lda * 2 >= lim || (int64_t)cf.bm * ldc * es >= lim) return false;
+    if (transb ? (int64_t)cf.bn * ldb * 2 >= lim : (int64_t)cf.bk * ldb * 2 >= lim) return false;
+    if (!transb && cf.bn / 8 < 16) return false;
+    return true;
+}
+
+int config_by_name(const char *name) {
+    for (int i = 0; i < kNumConfigs; ++i)
+        if (strcmp(kConfigs[i].name, name) == 0) return i;
+    return -1;
+}
+
+// Tile-configuration choice: the largest direct-to-LDS tile that still gives
+// at least one workgroup per CU (256), else the smallest; the register-staged
+// kernels for operands the direct path cannot address; the predicated kernel
+// for misaligned operands.
+int choose(int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb, int64_t ldc,
+           int c_type) {
     const int64_t b = batch < 1 ? 1 : batch;
-    if (cdiv(M, 256) * cdiv(N, 256) * b >= 256) return 0;
-    if (cdiv(M, 128) * cdiv(N, 128) * b >= 256) return 3;
-    return 4;
+    if (vec) {
+        const char *order[] = {"256x256x32_s3_w2x4_lds", "128x128x64_s2_w2x2_lds"};
+        for (int k = 0; k < 2; ++k) {
+            const int id = config_by_name(order[k]);
+            const Config &cf = kConfigs[id];
+            const bool enough = cdiv(M, cf.bm) * cdiv(N, cf.bn) * b >= 256 || k == 1;
+            if (enough && config_ok(cf, transb, vec, lda, ldb, ldc, c_type)) return id;
+        }
+        return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_vec" : "64x64x64_w2x2_vec");
+    }
+    return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_pred" : "64x64x64_w2x2_pred");
 }
 
 tdg_status validate(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
@@ -139,10 +179,12 @@ tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64
     const bool vec = vec_ok(transb, N, K, A, lda, sA, B, ldb, sB, batch);
     if (config < -1 || config >= kNumConfigs)
         return fail(TDG_INVALID_VALUE, "config %d out of range [-1, %d)", config, kNumConfigs);
-    if (config == -1) config = choose(vec, M, N, batch);
+    if (config == -1) config = choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type);
     const Config &cf = kConfigs[config];
     if (cf.vec && !vec)
         return fail(TDG_INVALID_VALUE, "config %s needs 16-byte aligned operands with 8-element granules", cf.name);
+    if (!config_ok(cf, transb, vec, lda, ldb, ldc, c_type))
+        return fail(TDG_INVALID_VALUE, "config %s cannot serve these leading dimensions or this layout", cf.name);
     st = check_device();
     if (st != TDG_SUCCESS) return st;
 
@@ -225,7 +267,7 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K, const void *A
                       ab_type, c_type, false) != TDG_SUCCESS)
         return -1;
     const bool vec = tdg::vec_ok(transb, N, K, A, lda, 0, B, ldb, 0, batch);
-    return tdg::choose(vec, M, N, batch);
+    return tdg::choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type);
 }
 
 const char *tdg_status_string(tdg_status status) {
