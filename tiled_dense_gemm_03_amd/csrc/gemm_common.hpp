@@ -26,14 +26,13 @@ struct GemmArgs {
 // (BK 64, two stages), VEC = vectorised loads (aligned operands) or the
 // predicated element-load path (any operands).
 #define TDG_CONFIG_LIST(X)                                                   \
-    X(0, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
-    X(1, 1, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_lds")           \
-    X(2, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
-    X(3, 1, 256, 256, 32, 4, 2, 2, true, "256x256x32_s4_w2x2_lds")           \
-    X(4, 1, 256, 128, 64, 3, 2, 2, true, "256x128x64_s3_w2x2_lds")           \
-    X(5, 1, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_lds")           \
-    X(6, 1, 128, 128, 32, 4, 2, 2, true, "128x128x32_s4_w2x2_lds")           \
-    X(7, 0, 128, 128, 64, 2, 2, 2, true, "128x128x64_w2x2_vec")              \
-    X(8, 0, 64, 64, 64, 2, 2, 2, true, "64x64x64_w2x2_vec")                  \
-    X(9, 0, 64, 64, 64, 2, 2, 2, false, "64x64x64_w2x2_pred")                \
-    X(10, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")
+    X(0, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
+    X(1, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
+    X(2, 1, 256, 256, 32, 3, 2, 2, true, "256x256x32_s3_w2x2_lds")           \
+    X(3, 1, 256, 128, 64, 2, 2, 2, true, "256x128x64_s2_w2x2_lds")           \
+    X(4, 1, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_lds")           \
+    X(5, 1, 128, 128, 32, 4, 2, 2, true, "128x128x32_s4_w2x2_lds")           \
+    X(6, 0, 128, 128, 64, 2, 2, 2, true, "128x128x64_w2x2_vec")              \
+    X(7, 0, 64, 64, 64, 2, 2, 2, true, "64x64x64_w2x2_vec")                  \
+    X(8, 0, 64, 64, 64, 2, 2, 2, false, "64x64x64_w2x2_pred")                \
+    X(9, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")

@@ -6,12 +6,13 @@
 //
 //  * Direct global -> LDS loads in buffer form (buffer_load_dwordx4 ... lds).
 //    Lane l of an instruction writes its 16 bytes at LDS base + 16*l, so the
-//    swizzled LDS layout is produced by choosing, for each LDS slot, which
-//    global granule its lane fetches.  A lane whose element lies outside the
-//    matrix uses an offset past the buffer's range: the hardware skips the
-//    memory access and writes zeros, which is exactly the zero-filled masked
-//    read of the primer's s5, with no branch and no staging registers.
-//  * v_mfma_f32_32x32x16_{f16,bf16} with AccVGPR accumulators.
+//    LDS layout is produced by choosing, for each LDS slot, which global
+//    granule its lane fetches.  A lane whose slot is padding or whose element
+//    lies outside the matrix uses an offset past the buffer's range: the
+//    hardware skips the memory access and writes zeros, which is exactly the
+//    zero-filled masked read of the primer's s5, with no branch and no staging
+//    registers.
+//  * v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulators.
 //  * ds_read_b64_tr_b16 for the B operand of NN products: B stays N-contiguous
 //    in LDS (as it is in memory) and the transposing LDS read delivers the
 //    K-runs the MFMA B operand wants.  Within each 16-lane group, result lane
@@ -26,17 +27,19 @@
 //   B of NN:         [BK k][BN/8 granules], N-contiguous; granule c of row k
 //                    at position c ^ (4 * (k & 3)).
 // Each XOR puts the 16 granules that 16 neighbouring lanes read at once on 16
-// distinct 16-byte bank groups (the LDS has 64 four-byte banks), so the
-// operand reads are conflict-free; the direct loads write 1 KiB contiguous
-// runs.  Writer and reader derive positions from the same formulas (the
-// Croqtile tutorial ch.4 notes that a swizzled store and the operand load
-// must agree on the swizzle).
+// distinct 16-byte bank groups (the LDS has 64 four-byte banks), so operand
+// reads are conflict-free, while every stage stays a whole number of 1 KiB
+// direct-load runs with no padding.  The XOR terms are such that each
+// operand needs only a few base addresses per lane (the rest are
+// compile-time offsets).  Writer and reader derive positions from the same
+// formulas (the Croqtile tutorial ch.4 notes that a swizzled store and the
+// operand load must agree on the swizzle).
 //
-// Pipeline: the STAGES LDS stages are separate objects, so the compiler can
-// prove that reading one stage never touches the direct loads in flight into
-// the others.  Loads run STAGES-1 tiles ahead; the fragments of K step kk+1
-// are read while the MFMAs of step kk run; the single barrier per K tile sits
-// before the tile's last step, whose fragments are already in registers.
+// Pipeline: the STAGES LDS stages are separate objects.  Loads run STAGES-1
+// tiles ahead; the fragments of K step kk+1 are read while the MFMAs of step
+// kk run; the single barrier per K tile sits before the tile's last step,
+// whose fragments are already in registers, and the refill of the freed stage
+// is spread between that step's MFMAs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,7 +53,6 @@
 namespace tdg {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;    // >= num_records: load returns zeros
 constexpr int32_t BUF_RECORDS = 0x7fffffff;     // every valid offset is below 2^31
@@ -78,20 +80,63 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base) {
 // from another here, does not add a wait for these loads before every LDS
 // read; the kernel waits for them explicitly (vmcnt) before its barriers.
 // M0 (which holds the LDS address) is saved and restored around the load.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+// The LDS address is lds_base + IMM (IMM a compile-time byte offset), so a
+// whole stage needs a single address register.
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
+        "s_add_u32 m0, %3, %4\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(lds_addr)
-        : "memory");
+        : "v"(voff), "s"(rsrc), "s"(lds_base), "n"(IMM)
+        : "memory", "scc");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most VM vector memory
+// operations are outstanding and every LDS operation has completed.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+
+// Order the instructions of one compute block: MF MFMAs with DS LDS reads
+// spread between them, PER MFMAs before each read (a scheduling constraint
+// only; it changes no result).
+template <int MF, int DS, int PER>
+__device__ __forceinline__ void interleave_rec() {
+    if constexpr (MF > 0 || DS > 0) {
+        constexpr int take = MF < PER ? MF : PER;
+        if constexpr (take > 0) __builtin_amdgcn_sched_group_barrier(0x008, take, 0);
+        if constexpr (DS > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            interleave_rec<MF - take, DS - 1, PER>();
+        } else {
+            interleave_rec<MF - take, 0, PER>();
+        }
+    }
+}
+
+template <int NMF, int NDS>
+__device__ __forceinline__ void interleave_hint() {
+    constexpr int PER = NDS > 0 ? (NMF > NDS ? NMF / NDS : 1) : NMF;
+    interleave_rec<NMF, NDS, PER>();
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // Position of granule g of row r in a K-contiguous tile with rows of BK.
@@ -105,83 +150,54 @@ __device__ __forceinline__ int kpos(int r, int g) {
 template <int BNG>
 __device__ __forceinline__ int npos(int k, int c) { return k * BNG + (c ^ (4 * (k & 3))); }
 
-// s_waitcnt immediate (gfx9 encoding): wait until at most VM vector memory
-// operations are outstanding and every LDS operation has completed.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-}
-
-// Order the instructions of one compute block: MF MFMAs with DS LDS reads
-// and VM direct global loads spread between them (LDS reads first), PER
-// MFMAs before each memory instruction (a scheduling constraint only; it
-// changes no result).
-template <int MF, int DS, int VM, int PER>
-__device__ __forceinline__ void interleave_rec() {
-    if constexpr (MF > 0 || DS > 0 || VM > 0) {
-        constexpr int take = MF < PER ? MF : PER;
-        if constexpr (take > 0) __builtin_amdgcn_sched_group_barrier(0x008, take, 0);
-        if constexpr (DS > 0) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            interleave_rec<MF - take, DS - 1, VM, PER>();
-        } else if constexpr (VM > 0) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            interleave_rec<MF - take, 0, VM - 1, PER>();
-        } else {
-            interleave_rec<MF - take, 0, 0, PER>();
-        }
-    }
-}
-
-template <int NMF, int NDS, int NVM>
-__device__ __forceinline__ void interleave_hint() {
-    constexpr int MEM = NDS + NVM;
-    constexpr int PER = MEM > 0 ? (NMF > MEM ? NMF / MEM : 1) : NMF;
-    interleave_rec<NMF, NDS, NVM, PER>();
-}
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
+// Tile geometry.
+template <int BM, int BN, int BK, int STAGES, bool TRANSB>
+struct FastGeom {
+    static constexpr int KG = BK / GRAN;                        // granules per K-contiguous row
+    static constexpr int BNG = BN / GRAN;                       // granules per NN B row
+    static constexpr int A_SLOTS = BM * KG;
+    static constexpr int B_SLOTS = BN * KG;                     // BK x BN either way
+    static constexpr int STAGE = A_SLOTS + B_SLOTS;             // granules per stage
+    // Direct loads are issued in whole-wave instructions; when a stage is not
+    // a multiple of one instruction per wave, the spare instructions write
+    // zeros into a 1 KiB scratch area so that every wave issues the same count.
+    template <int NW>
+    static constexpr bool needs_trash() { return (A_SLOTS / 64) % NW != 0 || (B_SLOTS / 64) % NW != 0; }
+    template <int NW>
+    static constexpr int lds_bytes() { return STAGE * 16 * STAGES + (needs_trash<NW>() ? 1024 : 0); }
+};
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool TRANSB, int AB, int CT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
-    constexpr int NT = WM * WN * 64, NW = WM * WN;
+    constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int RM = WTM / 32, RN = WTN / 32;
     static_assert(RM * 32 == WTM && RN * 32 == WTN, "wave tile must be a multiple of 32");
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
-    constexpr int KG = BK / GRAN;                    // granules per K-contiguous row
+    using G = FastGeom<BM, BN, BK, STAGES, TRANSB>;
     constexpr int KS = BK / 16;                      // MFMA K steps per tile
-    constexpr int A_SLOTS = BM * KG;                 // granules of one A stage
-    constexpr int B_SLOTS = BN * KG;                 // granules of one B stage (BK x BN either way)
-    constexpr int STAGE = A_SLOTS + B_SLOTS;
-    constexpr int A_INST = A_SLOTS / NT;             // direct loads per lane per stage
-    constexpr int B_INST = B_SLOTS / NT;
-    static_assert(A_INST * NT == A_SLOTS && B_INST * NT == B_SLOTS, "tile must split over the lanes");
-    constexpr int NDMA = A_INST + B_INST;
-    constexpr int BNG = BN / GRAN;                   // granules per NN B row
-    static_assert(TRANSB || BNG >= 16, "NN B swizzle needs rows of at least 16 granules");
+    constexpr int KG = G::KG, BNG = G::BNG;
+    constexpr int A_SLOTS = G::A_SLOTS, B_SLOTS = G::B_SLOTS, STAGE = G::STAGE;
+    static_assert(G::template lds_bytes<NW>() <= 160 * 1024, "LDS budget");
+    static_assert(TRANSB || BNG >= 16, "NN B rows of at least 16 granules");
+    static_assert(RM == 1 || WTM % 64 == 0, "A fragment bases assume 64-row wave tiles");
+    static_assert(!TRANSB || RN == 1 || WTN % 64 == 0, "B fragment bases assume 64-row wave tiles");
+    constexpr int NIA = A_SLOTS / 64, NIB = B_SLOTS / 64;     // wave-wide load instructions per stage
+    static_assert(NIA * 64 == A_SLOTS && NIB * 64 == B_SLOTS, "stage must be whole 1 KiB runs");
+    constexpr int QA = (NIA + NW - 1) / NW, QB = (NIB + NW - 1) / NW;   // per wave (the last may be idle)
+    constexpr int NDMA = QA + QB;
     static_assert((STAGES - 1) * NDMA < 64, "vmcnt range");
 
-    __shared__ u32x4 sm0[STAGE];
-    __shared__ u32x4 sm1[STAGE];
-    __shared__ u32x4 sm2[STAGES > 2 ? STAGE : 1];
-    __shared__ u32x4 sm3[STAGES > 3 ? STAGE : 1];
-    auto stage_ptr = [&](auto tag) -> u32x4 * {
-        constexpr int s = decltype(tag)::value;
-        if constexpr (s == 0) return sm0;
-        else if constexpr (s == 1) return sm1;
-        else if constexpr (s == 2) return sm2;
-        else return sm3;
-    };
+    // Stages back to back, then the 1 KiB scratch area for spare loads.  After
+    // the K loop the same memory stages the output tile (epilogue).
+    __shared__ u32x4 smem[STAGES * STAGE + (G::template needs_trash<NW>() ? 64 : 0)];
+    u32x4 *const trash = smem + STAGES * STAGE;
+    auto stage_ptr = [&](auto tag) -> u32x4 * { return smem + decltype(tag)::value * STAGE; };
+    u32x4 *const sm0 = stage_ptr(std::integral_constant<int, 0>{});
+    u32x4 *const sm1 = stage_ptr(std::integral_constant<int, 1>{});
+    u32x4 *const sm2 = stage_ptr(std::integral_constant<int, (STAGES > 2 ? 2 : 0)>{});
+    u32x4 *const sm3 = stage_ptr(std::integral_constant<int, (STAGES > 3 ? 3 : 0)>{});
 
     int batch, tm, tn;
     tile_coords(p, batch, tm, tn);
@@ -198,140 +214,118 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
                                    : p.B + (int64_t)batch * p.sB + n0;
 
     // ---- per-lane direct-load descriptors, fixed over the K loop ----
-    uint32_t a_off[A_INST];
-    int a_klim[A_INST];      // loaded while k0 < a_klim (K - 8g; -1 if the row is outside)
+    // Load instruction t = wave + NW*q writes LDS slots 64t .. 64t+63 of the
+    // stage; the lane fetches the global granule that the layout puts in its
+    // slot (the XOR swizzles are involutions), or, if that granule's row lies
+    // outside the matrix, uses the out-of-range offset.  klim: the granule is
+    // loaded while k0 < klim.
+    uint32_t a_off[QA];
+    int a_klim[QA];
 #pragma unroll
-    for (int q = 0; q < A_INST; ++q) {
+    for (int q = 0; q < QA; ++q) {
         const int slot = (q * NW + wave) * 64 + lane;
-        const int row = slot / KG, phys = slot % KG;
-        const int g = kpos<BK>(row, phys) - row * KG;   // the XOR is an involution
-        a_off[q] = (uint32_t)(row * p.lda + g * GRAN) * 2u;
-        a_klim[q] = (m0 + row < M) ? K - g * GRAN : -1;
+        const int row = slot / KG;
+        const int g = kpos<BK>(row, slot % KG) - row * KG;
+        const bool ok = m0 + row < M;
+        a_off[q] = ok ? (uint32_t)(row * p.lda + g * GRAN) * 2u : OOB_OFFSET;
+        a_klim[q] = ok ? K - g * GRAN : -1;
     }
-    uint32_t b_off[B_INST];
-    int b_klim[B_INST];
+    uint32_t b_off[QB];
+    int b_klim[QB];
 #pragma unroll
-    for (int q = 0; q < B_INST; ++q) {
+    for (int q = 0; q < QB; ++q) {
         const int slot = (q * NW + wave) * 64 + lane;
         if constexpr (TRANSB) {
-            const int row = slot / KG, phys = slot % KG;
-            const int g = kpos<BK>(row, phys) - row * KG;
-            b_off[q] = (uint32_t)(row * p.ldb + g * GRAN) * 2u;
-            b_klim[q] = (n0 + row < N) ? K - g * GRAN : -1;
+            const int row = slot / KG;
+            const int g = kpos<BK>(row, slot % KG) - row * KG;
+            const bool ok = n0 + row < N;
+            b_off[q] = ok ? (uint32_t)(row * p.ldb + g * GRAN) * 2u : OOB_OFFSET;
+            b_klim[q] = ok ? K - g * GRAN : -1;
         } else {
-            const int k = slot / BNG, phys = slot % BNG;
-            const int c = npos<BNG>(k, phys) - k * BNG;
-            b_off[q] = (uint32_t)(k * p.ldb + c * GRAN) * 2u;
-            b_klim[q] = (n0 + c * GRAN < N) ? K - k : -1;
+            const int k = slot / BNG;
+            const int c = npos<BNG>(k, slot % BNG) - k * BNG;
+            const bool ok = n0 + c * GRAN < N;
+            b_off[q] = ok ? (uint32_t)(k * p.ldb + c * GRAN) * 2u : OOB_OFFSET;
+            b_klim[q] = ok ? K - k : -1;
         }
     }
 
-    // Enqueue the direct loads of K tile kt into the stage at sa.
-    auto issue_to = [&](int kt, u32x4 *sa) {
-        const int k0 = kt * BK;
-        const u32x4 ra = rsrc_words(Atile + k0);
-        const u32x4 rb = rsrc_words(TRANSB ? Btile + k0 : Btile + (int64_t)k0 * p.ldb);
-        const uint32_t la = lds_addr_of(sa) + (uint32_t)wave * 1024u;
-        const uint32_t lb = la + A_SLOTS * 16u;
-#pragma unroll
-        for (int q = 0; q < A_INST; ++q) {
-            const uint32_t off = (k0 < a_klim[q]) ? a_off[q] : OOB_OFFSET;
-            dma16(ra, off, la + q * NW * 1024u);
-        }
-#pragma unroll
-        for (int q = 0; q < B_INST; ++q) {
-            const uint32_t off = (k0 < b_klim[q]) ? b_off[q] : OOB_OFFSET;
-            dma16(rb, off, lb + q * NW * 1024u);
-        }
-    };
-
-    // Direct load number q (0 <= q < NDMA) of K tile kt into the stage at sa.
+    // Direct load number q (0 <= q < NDMA) of this wave for K tile kt into
+    // the stage at sa.  Every wave issues NDMA loads per tile (spare ones go
+    // to the scratch area with an out-of-range offset), so one vmcnt value
+    // fits all waves.
     auto dma_op = [&](auto qtag, int kt, u32x4 *sa) {
         constexpr int q = decltype(qtag)::value;
         const int k0 = kt * BK;
-        const uint32_t la = lds_addr_of(sa) + (uint32_t)wave * 1024u;
-        if constexpr (q < A_INST) {
-            const uint32_t off = (k0 < a_klim[q]) ? a_off[q] : OOB_OFFSET;
-            dma16(rsrc_words(Atile + k0), off, la + q * NW * 1024u);
+        // wave-relative base of this stage; spare loads go to the scratch
+        // area (whose offset from the stage is fixed at link time, so it is
+        // folded into the same base)
+        const uint32_t base = lds_addr_of(sa) + (uint32_t)wave * 1024u;
+        if constexpr (q < QA) {
+            const bool live = NIA % NW == 0 || q * NW + wave < NIA;
+            const uint32_t off = (live && k0 < a_klim[q]) ? a_off[q] : OOB_OFFSET;
+            const uint32_t dst = live ? base : lds_addr_of(trash) - (uint32_t)(q * NW) * 1024u;
+            dma16<(uint32_t)(q * NW) * 1024u>(rsrc_words(Atile + k0), off, dst);
         } else {
-            constexpr int qb = q - A_INST;
-            const uint32_t off = (k0 < b_klim[qb]) ? b_off[qb] : OOB_OFFSET;
-            dma16(rsrc_words(TRANSB ? Btile + k0 : Btile + (int64_t)k0 * p.ldb), off,
-                  la + A_SLOTS * 16u + qb * NW * 1024u);
+            constexpr int qb = q - QA;
+            const bool live = NIB % NW == 0 || qb * NW + wave < NIB;
+            const uint32_t off = (live && k0 < b_klim[qb]) ? b_off[qb] : OOB_OFFSET;
+            const uint32_t dst = live ? base : lds_addr_of(trash) - (uint32_t)(A_SLOTS * 16 + qb * NW * 1024);
+            dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(
+                rsrc_words(TRANSB ? Btile + k0 : Btile + (int64_t)k0 * p.ldb), off, dst);
         }
     };
+    auto issue_to = [&](int kt, u32x4 *sa) { static_for<0, NDMA>([&](auto q) { dma_op(q, kt, sa); }); };
 
-    // ---- fragment addresses within a stage (granules for b128 reads, bytes
-    // for the NN B transposing reads) ----
+    // ---- fragment addresses: a few bases per lane plus constant offsets ----
+    // A (and TN B) fragment i at K step kk: granule 2 kk + frag_g of row
+    // wave_x * WT + 32 i + frag_row.  Rows 64 apart share the XOR term, so
+    // fragment i uses base i % 2 plus 32 * (i - i % 2) rows.
     const int frag_row = lane & 31;
     const int frag_g = lane >> 5;
-    int a_frag[RM][KS];
+    int a_b[2][KS], bt_b[2][KS];
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) a_frag[i][kk] = kpos<BK>(wave_m * WTM + i * 32 + frag_row, kk * 2 + frag_g);
-    int b_frag[RN][KS][TRANSB ? 1 : 2];
-#pragma unroll
-    for (int j = 0; j < RN; ++j)
+    for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            if constexpr (TRANSB) {
-                b_frag[j][kk][0] = kpos<BK>(wave_n * WTN + j * 32 + frag_row, kk * 2 + frag_g);
-            } else {
-                const int grp = lane >> 4, pos = lane & 15;
-                const int jr = pos >> 2, q4 = pos & 3;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = kk * 16 + 8 * (grp >> 1) + 4 * h + jr;
-                    const int n = wave_n * WTN + j * 32 + 16 * (grp & 1) + 4 * q4;
-                    const int c = n / GRAN, half = (n % GRAN) / 4;
-                    b_frag[j][kk][h] = npos<BNG>(k, c) * 16 + half * 8;
-                }
-            }
+            a_b[v][kk] = kpos<BK>(wave_m * WTM + 32 * v + frag_row, 2 * kk + frag_g);
+            bt_b[v][kk] = kpos<BK>(wave_n * WTN + 32 * v + frag_row, 2 * kk + frag_g);
         }
-
-    // MFMA operand fragments of K step kk from the stage at sa.
-    auto frags_from = [&](const u32x4 *sa, int kk, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
-        const u32x4 *sb = sa + A_SLOTS;
+    // NN B: byte address of the 8-byte piece lane `lane` supplies to tr read h
+    // of column block j at K step kk: row 16 kk + 8 (grp >> 1) + 4 h + jr,
+    // columns wave_n * WTN + 32 j + 16 (grp & 1) + 4 q4 .. +3.  The XOR term
+    // depends on the row only through jr, so (kk, h) are constant offsets.
+    const int grp = lane >> 4, jr = (lane & 15) >> 2, q4 = lane & 3;
+    int bn_b[RN];
 #pragma unroll
-        for (int i = 0; i < RM; ++i) af[i] = sa[a_frag[i][kk]];
-#pragma unroll
-        for (int j = 0; j < RN; ++j) {
-            if constexpr (TRANSB) {
-                bf[j] = sb[b_frag[j][kk][0]];
-            } else {
-                const char *base = reinterpret_cast<const char *>(sb);
-                s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(base + b_frag[j][kk][0]));
-                s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(base + b_frag[j][kk][1]));
-                u32x4 v;
-                v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-                v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-                v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-                v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-                bf[j] = v;
-            }
-        }
-    };
+    for (int j = 0; j < RN; ++j) {
+        const int n = wave_n * WTN + 32 * j + 16 * (grp & 1) + 4 * q4;
+        bn_b[j] = npos<BNG>(8 * (grp >> 1) + jr, n / GRAN) * 16 + ((n % GRAN) / 4) * 8;
+    }
 
-    // LDS read number d (0 <= d < RM + RN or RM + 2 RN) of K step kk's fragments.
+    // LDS read number d (0 <= d < NDS) of K step kk's fragments.
     auto frag_op = [&](auto dtag, const u32x4 *sa, int kk, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
         constexpr int d = decltype(dtag)::value;
         const u32x4 *sb = sa + A_SLOTS;
         if constexpr (d < RM) {
-            af[d] = sa[a_frag[d][kk]];
+            af[d] = sa[a_b[d & 1][kk] + (d & ~1) * 32 * KG];
         } else if constexpr (TRANSB) {
-            bf[d - RM] = sb[b_frag[d - RM][kk][0]];
+            constexpr int j = d - RM;
+            bf[j] = sb[bt_b[j & 1][kk] + (j & ~1) * 32 * KG];
         } else {
             constexpr int j = (d - RM) / 2, h = (d - RM) % 2;
             const char *base = reinterpret_cast<const char *>(sb);
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(base + b_frag[j][kk][h]));
+                (__attribute__((address_space(3))) s16x4 *)(base + bn_b[j] + (16 * kk + 4 * h) * BNG * 16));
             const uint64_t w = __builtin_bit_cast(uint64_t, v);
             bf[j][2 * h] = (uint32_t)w;
             bf[j][2 * h + 1] = (uint32_t)(w >> 32);
         }
+    };
+    constexpr int NDS = RM + (TRANSB ? RN : 2 * RN);   // LDS reads per K step
+    constexpr int NMF = RM * RN;                       // MFMAs per K step
+    auto frags_from = [&](const u32x4 *sa, int kk, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
+        static_for<0, NDS>([&](auto d) { frag_op(d, sa, kk, af, bf); });
     };
 
     f32x16 acc[RM][RN];
@@ -342,8 +336,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    constexpr int NDS = RM + (TRANSB ? RN : 2 * RN);   // LDS reads per K step
-    constexpr int NMF = RM * RN;                       // MFMAs per K step
     const int nk = (K + BK - 1) / BK;
     u32x4 af[2][RM], bf[2][RN];
 
@@ -372,8 +364,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
             for (int i = 0; i < RM; ++i)
 #pragma unroll
                 for (int j = 0; j < RN; ++j)
-                    acc[i][j] = mfma_32x32x16<AB>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
-            interleave_hint<NMF, NDS, 0>();
+                    acc[i][j] = mfma_32x32x16<AB>(bf[kk & 1][j], af[kk & 1][i], acc[i][j]);
+            interleave_hint<NMF, NDS>();
         }
         // Tile kt+1 has landed (tiles kt+2 .. kt+STAGES-1 may still be in
         // flight) and this lane's reads of stage S are done; after the
@@ -390,7 +382,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
             constexpr int s0 = decltype(sub)::value;
             static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
                 constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
-                acc[i][j] = mfma_32x32x16<AB>(af[(KS - 1) & 1][i], bf[(KS - 1) & 1][j], acc[i][j]);
+                acc[i][j] = mfma_32x32x16<AB>(bf[(KS - 1) & 1][j], af[(KS - 1) & 1][i], acc[i][j]);
             });
             static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>([&](auto d) {
                 frag_op(d, nxt, 0, af[KS & 1], bf[KS & 1]);
@@ -411,32 +403,98 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(0);   // the trailing out-of-range loads have retired
 
-    // ---- epilogue: fp32 -> output type; out-of-range elements are dropped by
-    // the buffer range check (store mask of the primer's s5) ----
+    // ---- epilogue: fp32 -> output type, store mask of the primer's s5 ----
+    // The MFMAs take B as their first operand, so accumulator register
+    // 4g + e of lane l holds C[m, n] with m = l % 32 and n = 8g + 4(l / 32) + e
+    // inside each 32 x 32 block: four consecutive columns per lane.  Rows past
+    // M use an out-of-range offset (dropped by the buffer range check).  Tiles
+    // that reach past N, or a C whose rows are not 4-byte aligned, take the
+    // element-wise path.
     constexpr int ES = (CT == OUT_F32) ? 4 : 2;
     const char *Cbase = (const char *)p.C + ((int64_t)batch * p.sC + (int64_t)m0 * p.ldc + n0) * ES;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase);
-    const int col_l = lane & 31;
-    const int row_l = 4 * (lane >> 5);
+    const int ml = lane & 31;
+    const int nl = 4 * (lane >> 5);
+    const bool vec_store = (n0 + BN <= N) && (((uintptr_t)p.C | (uintptr_t)(p.ldc * ES) | (uintptr_t)(p.sC * ES)) & 3) == 0;
+    if (vec_store) {
+        // Through LDS, one 32-row block of the wave's sub-tile at a time, so
+        // that every global store instruction writes whole row segments:
+        // lanes write their four consecutive columns into a row-major block
+        // (rows padded by 16 bytes, an odd number of granules, so the 16 rows
+        // written at once hit distinct banks), then read it back 16 bytes per
+        // lane along the rows and store.
+        constexpr int ROWB = WTN * ES + 16;                 // bytes per staged row
+        constexpr int CPR = WTN * ES / 16;                  // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;                       // rows per read instruction
+        static_assert(RPI * CPR == 64 && 32 % RPI == 0, "row chunks must tile a wave");
+        static_assert(NW * 32 * ROWB <= STAGES * STAGE * 16, "epilogue staging fits in LDS");
+        __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        char *const region = reinterpret_cast<char *>(smem) + wave * 32 * ROWB;
 #pragma unroll
-    for (int i = 0; i < RM; ++i) {
+        for (int i = 0; i < RM; ++i) {
 #pragma unroll
-        for (int j = 0; j < RN; ++j) {
-            // one 32 x 32 tile at a time: keeps the conversion temporaries few
-            __builtin_amdgcn_sched_barrier(0);
-            const int cn = wave_n * WTN + j * 32 + col_l;
-            const bool col_ok = n0 + cn < N;
+            for (int j = 0; j < RN; ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int cm = wave_m * WTM + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
-                const uint32_t off = (col_ok && m0 + cm < M) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
-                const float v = acc[i][j][r];
-                if constexpr (CT == OUT_F32) {
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, off, 0, 0);
-                } else if constexpr (CT == OUT_F16) {
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), rc, off, 0, 0);
-                } else {
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc, off, 0, 0);
+                for (int g = 0; g < 4; ++g) {
+                    char *dst = region + ml * ROWB + (j * 32 + 8 * g + nl) * ES;
+                    const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+                    const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                    if constexpr (CT == OUT_F32) {
+                        u32x4 w;
+                        w[0] = __builtin_bit_cast(uint32_t, v0);
+                        w[1] = __builtin_bit_cast(uint32_t, v1);
+                        w[2] = __builtin_bit_cast(uint32_t, v2);
+                        w[3] = __builtin_bit_cast(uint32_t, v3);
+                        *reinterpret_cast<u32x4 *>(dst) = w;
+                    } else {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        u32x2 w;
+                        if constexpr (CT == OUT_F16) {
+                            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+                            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
+                        } else {
+                            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
+                            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
+                        }
+                        *reinterpret_cast<u32x2 *>(dst) = w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 32 / RPI; ++t) {
+                const int row = t * RPI + lane / CPR, chunk = lane % CPR;
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(region + row * ROWB + chunk * 16);
+                const int cm = wave_m * WTM + i * 32 + row;
+                const int cn = wave_n * WTN + chunk * 16 / ES;
+                const uint32_t off = (m0 + cm < M) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
+                __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RM; ++i) {
+            const int cm = wave_m * WTM + i * 32 + ml;
+            const bool row_ok = m0 + cm < M;
+#pragma unroll
+            for (int j = 0; j < RN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int cn = wave_n * WTN + j * 32 + 8 * (r >> 2) + nl + (r & 3);
+                    const uint32_t off = (row_ok && n0 + cn < N) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
+                    const float v = acc[i][j][r];
+                    if constexpr (CT == OUT_F32) {
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, off, 0, 0);
+                    } else if constexpr (CT == OUT_F16) {
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), rc, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc, off, 0, 0);
+                    }
                 }
             }
         }

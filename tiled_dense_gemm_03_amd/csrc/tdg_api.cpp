@@ -118,21 +118,22 @@ int config_by_name(const char *name) {
     return -1;
 }
 
-// Tile-configuration choice: the largest direct-to-LDS tile that still gives
-// at least one workgroup per CU (256), else the smallest; the register-staged
-// kernels for operands the direct path cannot address; the predicated kernel
-// for misaligned operands.
+// Tile-configuration choice (measured on MI355X): 256 x 256 tiles when the
+// problem has at least one tile per CU (256), with 64-wide K tiles and two
+// stages when there are two or more tiles per CU, 32-wide K tiles and three
+// stages otherwise; 128 x 128 tiles for smaller problems; the
+// register-staged kernel when the direct-load kernel cannot address the
+// operands; the predicated kernel for misaligned operands.
 int choose(int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb, int64_t ldc,
            int c_type) {
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
-        const char *order[] = {"256x256x32_s3_w2x4_lds", "128x128x64_s2_w2x2_lds"};
-        for (int k = 0; k < 2; ++k) {
-            const int id = config_by_name(order[k]);
-            const Config &cf = kConfigs[id];
-            const bool enough = cdiv(M, cf.bm) * cdiv(N, cf.bn) * b >= 256 || k == 1;
-            if (enough && config_ok(cf, transb, vec, lda, ldb, ldc, c_type)) return id;
-        }
+        const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
+        const char *first = tiles256 >= 512 ? "256x256x64_s2_w2x4_lds" : "256x256x32_s3_w2x4_lds";
+        const int id = config_by_name(first);
+        if (tiles256 >= 256 && config_ok(kConfigs[id], transb, vec, lda, ldb, ldc, c_type)) return id;
+        const int small = config_by_name("128x128x64_s2_w2x2_lds");
+        if (config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) return small;
         return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_vec" : "64x64x64_w2x2_vec");
     }
     return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_pred" : "64x64x64_w2x2_pred");
