@@ -24,7 +24,8 @@ struct GemmArgs {
 // waves.  KIND 1 = the direct-to-LDS kernel (aligned operands only) with K
 // tiles of BK and ST pipeline stages; KIND 0 = the register-staged kernel
 // (BK 64, two stages), VEC = vectorised loads (aligned operands) or the
-// predicated element-load path (any operands).
+// predicated element-load path (any operands); KIND 2 = the direct-to-LDS
+// kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64).
 #define TDG_CONFIG_LIST(X)                                                   \
     X(0, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
     X(1, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
@@ -35,4 +36,5 @@ struct GemmArgs {
     X(6, 0, 128, 128, 64, 2, 2, 2, true, "128x128x64_w2x2_vec")              \
     X(7, 0, 64, 64, 64, 2, 2, 2, true, "64x64x64_w2x2_vec")                  \
     X(8, 0, 64, 64, 64, 2, 2, 2, false, "64x64x64_w2x2_pred")                \
-    X(9, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")
+    X(9, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")           \
+    X(10, 2, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16")

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
     constexpr int RM = WTM / 32, RN = WTN / 32;
     static_assert(RM * 32 == WTM && RN * 32 == WTN, "wave tile must be a multiple of 32");
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+    static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
     using G = FastGeom<BM, BN, BK, STAGES, TRANSB>;
     constexpr int KS = BK / 16;                      // MFMA K steps per tile
     constexpr int KG = G::KG, BNG = G::BNG;
@@ -194,10 +194,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
     __shared__ u32x4 smem[STAGES * STAGE + (G::template needs_trash<NW>() ? 64 : 0)];
     u32x4 *const trash = smem + STAGES * STAGE;
     auto stage_ptr = [&](auto tag) -> u32x4 * { return smem + decltype(tag)::value * STAGE; };
-    u32x4 *const sm0 = stage_ptr(std::integral_constant<int, 0>{});
-    u32x4 *const sm1 = stage_ptr(std::integral_constant<int, 1>{});
-    u32x4 *const sm2 = stage_ptr(std::integral_constant<int, (STAGES > 2 ? 2 : 0)>{});
-    u32x4 *const sm3 = stage_ptr(std::integral_constant<int, (STAGES > 3 ? 3 : 0)>{});
 
     int batch, tm, tn;
     tile_coords(p, batch, tm, tn);
@@ -342,14 +338,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
     // Loads of tiles past the last one are all out of range: they fetch
     // nothing and only write zeros into a stage that is never read again.
     if (nk > 0) {
-        issue_to(0, sm0);
-        issue_to(1, sm1);
-        if constexpr (STAGES > 2) issue_to(2, sm2);
-        if constexpr (STAGES > 3) issue_to(3, sm3);
+        static_for<0, STAGES>([&](auto s) { issue_to(decltype(s)::value, stage_ptr(s)); });
         wait_vm_lgkm0<(STAGES - 1) * NDMA>();    // tile 0 has landed (this lane)
         __builtin_amdgcn_s_barrier();             // ... for every lane
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        frags_from(sm0, 0, af[0], bf[0]);
+        frags_from(smem, 0, af[0], bf[0]);
     }
 
     // One K tile held in stage S (a compile-time constant).
@@ -392,14 +385,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
         });
     };
     for (int kt = 0; kt < nk; kt += STAGES) {
-        tile_iter(std::integral_constant<int, 0>{}, kt);
-        if (kt + 1 < nk) tile_iter(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (STAGES > 2) {
-            if (kt + 2 < nk) tile_iter(std::integral_constant<int, 2>{}, kt + 2);
-        }
-        if constexpr (STAGES > 3) {
-            if (kt + 3 < nk) tile_iter(std::integral_constant<int, 3>{}, kt + 3);
-        }
+        static_for<0, STAGES>([&](auto s) {
+            constexpr int S = decltype(s)::value;
+            if (S == 0 || kt + S < nk) tile_iter(s, kt + S);
+        });
     }
     __builtin_amdgcn_s_waitcnt(0);   // the trailing out-of-range loads have retired
 

@@ -3,6 +3,7 @@
 // instantiations build in parallel.  Exposes one launcher per pair.
 #include "gemm_fast.hpp"
 #include "gemm_kernel.hpp"
+#include "gemm_m16.hpp"
 
 #ifndef TDG_TRANSB
 #error "TDG_TRANSB must be defined"
@@ -18,6 +19,10 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
     if constexpr (KIND == 1) {
         hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WM, WN, BK, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
+    } else if constexpr (KIND == 2) {
+        static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
+        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
+                           dim3(WM * WN * 64), 0, s, a);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, CT, VEC>), dim3((unsigned)grid),
                            dim3(NTHREADS), 0, s, a);
@@ -27,8 +32,8 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
 template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool VEC>
 static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     constexpr bool TB = TDG_TRANSB != 0;
-    if constexpr (KIND == 1 && !TB && BN / 8 < 16) {
-        return hipErrorInvalidValue;   // NN direct-to-LDS kernel needs BN >= 128
+    if constexpr (KIND >= 1 && !TB && BN / 8 < 16) {
+        return hipErrorInvalidValue;   // NN direct-to-LDS kernels need BN >= 128
     } else {
         switch (ct) {
         case OUT_F16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_F16, VEC>(a, grid, s); break;

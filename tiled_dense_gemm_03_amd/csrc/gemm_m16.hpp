@@ -1,0 +1,345 @@
+// gemm_m16.hpp -- MFMA 16x16x32 GEMM kernel for gfx950 (aligned operands).
+//
+// The same decomposition as the other kernels (one workgroup per output
+// tile, the K loop inside the workgroup, fp32 accumulators; NineToothed GEMM
+// primer s4 and s6), built for large wave tiles:
+//
+//  * v_mfma_f32_16x16x32_{f16,bf16}.  Lane l supplies row l % 16 of an
+//    operand and the 8 consecutive k values 8*(l / 16) .. +7; the 4 results
+//    of lane l are rows 4*(l / 16) + r (r = 0..3) of column l % 16.  The
+//    kernel passes the B fragment as the first operand, so lane l ends with
+//    C[m = l % 16][n = 4*(l / 16) + r]: four consecutive output columns.
+//    4-register accumulators leave the register allocator free to place a
+//    128 x 128 wave tile (256 accumulator registers) in AccVGPRs.
+//  * Direct global -> LDS loads (buffer_load_dwordx4 ... lds) as in the
+//    other direct-load kernel, with leaner addressing: every load of a wave
+//    uses one of at most two per-lane byte offsets plus a uniform row offset,
+//    and rows past the matrix edge are cut off by the buffer's record count
+//    (the descriptor of each K tile ends at the last valid element), so the
+//    per-lane state is a handful of registers whatever the tile size.  The
+//    zero fill of out-of-range reads is the primer's s5 masked load.
+//  * K-tail: a granule whose first k is at or past K gets an out-of-range
+//    offset (A and TN-B); NN-B rows past K fall outside the record count.
+//
+// LDS layouts (16-byte granules of 8 elements):
+//   A, TN-B: [rows][8 granules], granule g of row r at r*8 + (g ^ ((r>>1)&7)).
+//            The 16 rows read at once by 16 lanes (same granule) land on 16
+//            distinct 16-byte bank groups; rows 16 apart share the pattern,
+//            so one base address per K step serves every fragment.
+//   NN-B:    [64 k][BN/8 granules], granule c of row k at
+//            k*BN/8 + (c ^ (4*(k&3) + 2*((k>>3)&1))).  A transposing read
+//            (ds_read_b64_tr_b16) touches 4 consecutive k rows and 2
+//            granules per 16 lanes; the 32 lanes of one LDS cycle take
+//            k rows 8 apart, which the (k>>3) term separates.
+// Writer and reader derive positions from the same functions (the Croqtile
+// tutorial ch.4 remarks that a swizzled store and the operand load must
+// agree on the swizzle).
+#pragma once
+
+#include "gemm_fast.hpp"
+
+namespace tdg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int AB>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (AB == AB_F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+// Buffer descriptor words with an explicit record count (bytes).
+__device__ __forceinline__ u32x4 rsrc_words_n(const void *base, uint32_t records) {
+    const uint64_t a = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(records);
+    r[3] = (uint32_t)BUF_FLAGS;
+    return r;
+}
+
+// Record count for `elems` valid elements (clamped to [0, 2^31 - 1]).
+__device__ __forceinline__ uint32_t records_of(int64_t elems) {
+    const int64_t b = elems * 2;
+    return b <= 0 ? 0u : (b >= (int64_t)BUF_RECORDS ? (uint32_t)BUF_RECORDS : (uint32_t)b);
+}
+
+__device__ __forceinline__ int kx16(int r) { return (r >> 1) & 7; }                 // K-contiguous XOR
+__device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }  // NN-B XOR
+
+// BM x BN workgroup tile, WM x WN waves of (BM/WM) x (BN/WN), K tiles of 64
+// in STAGES LDS stages.
+template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSB, int AB, int CT>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
+    constexpr int BK = 64, KS = 2, KG = 8, BNG = BN / GRAN;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int RM = WTM / 16, RN = WTN / 16;
+    static_assert(RM * 16 == WTM && RN * 16 == WTN, "wave tile must be a multiple of 16");
+    static_assert(NW % 2 == 0, "an even number of waves");
+    static_assert(TRANSB || (BNG >= 16 && (BNG & (BNG - 1)) == 0), "NN B rows: a power of two >= 16 granules");
+    constexpr int A_SLOTS = BM * KG, B_SLOTS = BN * KG, STAGE = A_SLOTS + B_SLOTS;
+    constexpr int NIA = A_SLOTS / 64, NIB = B_SLOTS / 64;
+    static_assert(NIA % NW == 0 && NIB % NW == 0, "whole load instructions per wave");
+    constexpr int QA = NIA / NW, QB = NIB / NW, NDMA = QA + QB;
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+    static_assert((STAGES - 1) * NDMA < 64, "vmcnt range");
+    static_assert(STAGE * 16 * STAGES <= 160 * 1024, "LDS budget");
+    // NN-B load instruction t covers k rows t*RPB .. +RPB-1; its XOR pattern
+    // repeats every NVB instructions of one wave.
+    constexpr int RPB = 64 / BNG;
+    constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
+
+    __shared__ u32x4 smem[STAGES * STAGE];
+    auto stage_ptr = [&](auto tag) -> u32x4 * { return smem + decltype(tag)::value * STAGE; };
+
+    int batch, tm, tn;
+    tile_coords(p, batch, tm, tn);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave / WN, wave_n = wave % WN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int64_t lda = p.lda, ldb = p.ldb;
+
+    const uint16_t *Atile = p.A + (int64_t)batch * p.sA + (int64_t)m0 * lda;
+    const uint16_t *Btile = TRANSB ? p.B + (int64_t)batch * p.sB + (int64_t)n0 * ldb
+                                   : p.B + (int64_t)batch * p.sB + n0;
+    const int a_rows = M - m0 < BM ? M - m0 : BM;
+    const int b_rows = N - n0 < BN ? N - n0 : BN;     // TN: valid B rows; NN: valid columns
+
+    // ---- direct-load addressing ----
+    // K-contiguous operand, load q of this wave = instruction t = q*NW + wave:
+    // LDS slots 64t .. 64t+63 = rows 8t .. 8t+7, 8 granules each.  The lane's
+    // row is 8t + lane/8 and its granule g = (lane%8) ^ kx16(row); kx16 does
+    // not depend on q (NW is even), so the byte offset is a_lane + q*a_qs.
+    const int kc_row = wave * 8 + (lane >> 3);
+    const int kc_g = (lane & 7) ^ kx16(kc_row);
+    const uint32_t a_lane = (uint32_t)((kc_row * lda + kc_g * GRAN) * 2);
+    const uint32_t a_qs = (uint32_t)(NW * 8 * lda * 2);
+    const int kc_klim = K - kc_g * GRAN;           // granule loaded while k0 < kc_klim
+    uint32_t b_lane[NVB];
+    uint32_t b_qs;
+    if constexpr (TRANSB) {
+        b_lane[0] = (uint32_t)((kc_row * ldb + kc_g * GRAN) * 2);
+        b_qs = (uint32_t)(NW * 8 * ldb * 2);
+    } else {
+        // NN-B instruction t covers k rows RPB*t .. ; the lane's k is
+        // RPB*t + lane / BNG and its column granule (lane % BNG) ^ nx16(k).
+#pragma unroll
+        for (int v = 0; v < NVB; ++v) {
+            const int kr = RPB * wave + lane / BNG;          // k row relative to instruction q = 0
+            const int k = RPB * (v * NW) + kr;
+            const int c = (lane % BNG) ^ nx16(k);
+            b_lane[v] = (n0 + c * GRAN < N) ? (uint32_t)((kr * ldb + c * GRAN) * 2) : OOB_OFFSET;
+        }
+        b_qs = (uint32_t)(NW * RPB * ldb * 2);
+    }
+
+    auto dma_op = [&](auto qtag, int kt, u32x4 *sa) {
+        constexpr int q = decltype(qtag)::value;
+        const int k0 = kt * BK;
+        const uint32_t base = lds_addr_of(sa) + (uint32_t)wave * 1024u;
+        if constexpr (q < QA) {
+            const u32x4 rs = rsrc_words_n(Atile + k0, records_of((int64_t)(a_rows - 1) * lda + K - k0));
+            const uint32_t off = (k0 < kc_klim ? a_lane : OOB_OFFSET) + (uint32_t)q * a_qs;
+            dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+        } else {
+            constexpr int qb = q - QA;
+            if constexpr (TRANSB) {
+                const u32x4 rs = rsrc_words_n(Btile + k0, records_of((int64_t)(b_rows - 1) * ldb + K - k0));
+                const uint32_t off = (k0 < kc_klim ? b_lane[0] : OOB_OFFSET) + (uint32_t)qb * b_qs;
+                dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
+            } else {
+                const u32x4 rs = rsrc_words_n(Btile + (int64_t)k0 * ldb,
+                                              records_of((int64_t)(K - k0 - 1) * ldb + (N - n0)));
+                const uint32_t off = b_lane[qb % NVB] + (uint32_t)qb * b_qs;
+                dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
+            }
+        }
+    };
+    auto issue_to = [&](int kt, u32x4 *sa) { static_for<0, NDMA>([&](auto q) { dma_op(q, kt, sa); }); };
+
+    // ---- fragment addresses ----
+    // A (and TN-B) fragment i at K step ks: row wave_x*WT + 16 i + lane%16,
+    // granule 4 ks + lane/16; kx16 of that row is (lane>>1)&7 for every i.
+    const int fr = lane & 15, fg = lane >> 4;
+    int a_b[KS], bt_b[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        a_b[ks] = (wave_m * WTM + fr) * KG + ((4 * ks + fg) ^ ((lane >> 1) & 7));
+        bt_b[ks] = (wave_n * WTN + fr) * KG + ((4 * ks + fg) ^ ((lane >> 1) & 7));
+    }
+    // NN-B fragment j, half h at K step ks: lane supplies the 8 bytes at k
+    // row 32 ks + 8 fg + 4 h + jr, columns wave_n*WTN + 16 j + 4 q4 .. +3;
+    // nx16 of that row is 4 jr + 2 (fg & 1) for every (ks, h), so (ks, h)
+    // are constant offsets.
+    const int jr = (lane & 15) >> 2, q4 = lane & 3;
+    int bn_b[TRANSB ? 1 : RN];
+    if constexpr (!TRANSB) {
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            const int c = (wave_n * WTN + 16 * j + 4 * q4) / GRAN;
+            bn_b[j] = ((8 * fg + jr) * BNG + (c ^ (4 * jr + 2 * (fg & 1)))) * 16 + (q4 & 1) * 8;
+        }
+    }
+
+    auto frag_op = [&](auto dtag, const u32x4 *sa, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
+        constexpr int d = decltype(dtag)::value;
+        const u32x4 *sb = sa + A_SLOTS;
+        if constexpr (d < RM) {
+            af[d] = sa[a_b[ks] + d * 16 * KG];
+        } else if constexpr (TRANSB) {
+            constexpr int j = d - RM;
+            bf[j] = sb[bt_b[ks] + j * 16 * KG];
+        } else {
+            constexpr int j = (d - RM) / 2, h = (d - RM) % 2;
+            const char *base = reinterpret_cast<const char *>(sb);
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(base + bn_b[j] + (32 * ks + 4 * h) * BNG * 16));
+            const uint64_t w = __builtin_bit_cast(uint64_t, v);
+            bf[j][2 * h] = (uint32_t)w;
+            bf[j][2 * h + 1] = (uint32_t)(w >> 32);
+        }
+    };
+    constexpr int NDS = RM + (TRANSB ? RN : 2 * RN);
+    constexpr int NMF = RM * RN;
+    auto frags_from = [&](const u32x4 *sa, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
+        static_for<0, NDS>([&](auto d) { frag_op(d, sa, ks, af, bf); });
+    };
+
+    f32x4 acc[RM][RN];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nk = (K + BK - 1) / BK;
+    u32x4 af[2][RM], bf[2][RN];
+
+    if (nk > 0) {
+        static_for<0, STAGES>([&](auto s) { issue_to(decltype(s)::value, stage_ptr(s)); });
+        wait_vm_lgkm0<(STAGES - 1) * NDMA>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        frags_from(smem, 0, af[0], bf[0]);
+    }
+
+    // One K tile per iteration, held in stage s_cur: step 0 (its MFMAs with
+    // step 1's fragment reads), then the barrier, then step 1's MFMAs
+    // interleaved with the next tile's step-0 fragment reads and the refill
+    // of stage s_cur.  The stage is a run-time index (one loop body, no
+    // per-stage copies of the code).
+    int s_cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
+        u32x4 *cur = smem + s_cur * STAGE;
+        u32x4 *nxt = smem + s_nxt * STAGE;
+        frags_from(cur, 1, af[1], bf[1]);
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[0][j], af[0][i], acc[i][j]);
+        interleave_hint<NMF, NDS>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vm_lgkm0<(STAGES - 2) * NDMA>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        constexpr int NSUB = NDMA;
+        static_for<0, NSUB>([&](auto sub) {
+            constexpr int s0 = decltype(sub)::value;
+            static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
+                constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                acc[i][j] = mfma_16x16x32<AB>(bf[1][j], af[1][i], acc[i][j]);
+            });
+            static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>([&](auto d) { frag_op(d, nxt, 0, af[0], bf[0]); });
+            dma_op(sub, kt + STAGES, cur);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        s_cur = s_nxt;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- epilogue: fp32 -> output type, store mask of the primer's s5 ----
+    // Lane l holds C[m][n] for m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
+    // One 16-row block of the wave's sub-tile at a time goes through the
+    // wave's own LDS region in fp32 (the accumulators are written as they
+    // are, so they never need to be copied out of the accumulator registers
+    // all at once); each lane then reads back 4 consecutive fp32 values of a
+    // row, converts them (round to nearest even) and stores them: whole row
+    // segments for interior tiles, element by element where the tile passes
+    // N or C is not 4-byte aligned.  Rows past M are never stored.
+    constexpr int ES = (CT == OUT_F32) ? 4 : 2;
+    constexpr int ROWB = WTN * 4 + 16;             // staged row: fp32, padded by 16 bytes
+    constexpr int CPR = WTN / 4;                   // 4-column chunks per row
+    constexpr int RPI = 64 / CPR;                  // rows per read-back instruction
+    static_assert(RPI * CPR == 64 && 16 % RPI == 0, "row chunks must tile a wave");
+    static_assert(NW * 16 * ROWB <= STAGES * STAGE * 16, "epilogue staging fits in LDS");
+    const char *Cbase = (const char *)p.C + ((int64_t)batch * p.sC + (int64_t)m0 * p.ldc + n0) * ES;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase);
+    const bool vec_store = (n0 + BN <= N) && (((uintptr_t)p.C | (uintptr_t)(p.ldc * ES) | (uintptr_t)(p.sC * ES)) & 3) == 0;
+    __builtin_amdgcn_s_barrier();                  // every wave is done with the stages
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    char *const region = reinterpret_cast<char *>(smem) + wave * 16 * ROWB;
+    const int wrow = lane & 15, wcol = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            *reinterpret_cast<f32x4 *>(region + wrow * ROWB + (16 * j + wcol) * 4) = acc[i][j];
+        }
+#pragma unroll
+        for (int t = 0; t < 16 / RPI; ++t) {
+            const int row = t * RPI + lane / CPR, chunk = lane % CPR;
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(region + row * ROWB + chunk * 16);
+            const int cm = wave_m * WTM + i * 16 + row;
+            const int cn = wave_n * WTN + chunk * 4;
+            const bool row_ok = m0 + cm < M;
+            if (vec_store) {
+                const uint32_t off = row_ok ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
+                if constexpr (CT == OUT_F32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                } else {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    u32x2 w;
+                    if constexpr (CT == OUT_F16) {
+                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+                    } else {
+                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t off = (row_ok && n0 + cn + r < N) ? (uint32_t)(cm * p.ldc + cn + r) * ES : OOB_OFFSET;
+                    if constexpr (CT == OUT_F32) {
+                        // (the words of the whole vector: hipcc's bit cast of a
+                        // single vector element reads element 0 whatever the index)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32x4, v)[r], rc, off, 0, 0);
+                    } else if constexpr (CT == OUT_F16) {
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v[r]), rc, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v[r]), rc, off, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace tdg

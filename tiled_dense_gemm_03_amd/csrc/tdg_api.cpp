@@ -97,7 +97,7 @@ bool vec_ok(int transb, int64_t N, int64_t K, const void *A, int64_t lda, int64_
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Whether configuration `cf` can serve the operands: the vectorised kinds
-// need vec_ok; the direct-to-LDS kind also needs every in-tile byte offset
+// need vec_ok; the direct-to-LDS kinds also need every in-tile byte offset
 // below 2^31 (buffer offsets are 32-bit) and, for NN, B rows of at least 16
 // granules in LDS.
 bool config_ok(const Config &cf, int transb, bool vec, int64_t lda, int64_t ldb, int64_t ldc, int c_type) {
@@ -118,19 +118,17 @@ int config_by_name(const char *name) {
     return -1;
 }
 
-// Tile-configuration choice (measured on MI355X): 256 x 256 tiles when the
-// problem has at least one tile per CU (256), with 64-wide K tiles and two
-// stages when there are two or more tiles per CU, 32-wide K tiles and three
-// stages otherwise; 128 x 128 tiles for smaller problems; the
-// register-staged kernel when the direct-load kernel cannot address the
-// operands; the predicated kernel for misaligned operands.
+// Tile-configuration choice (measured on MI355X): 256 x 256 tiles on the
+// 16 x 16 x 32 MFMA kernel when the problem has at least one tile per CU
+// (256); 128 x 128 tiles for smaller problems; the register-staged kernel
+// when the direct-load kernels cannot address the operands; the predicated
+// kernel for misaligned operands.
 int choose(int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb, int64_t ldc,
            int c_type) {
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
-        const char *first = tiles256 >= 512 ? "256x256x64_s2_w2x4_lds" : "256x256x32_s3_w2x4_lds";
-        const int id = config_by_name(first);
+        const int id = config_by_name("256x256x64_s2_w2x4_m16");
         if (tiles256 >= 256 && config_ok(kConfigs[id], transb, vec, lda, ldb, ldc, c_type)) return id;
         const int small = config_by_name("128x128x64_s2_w2x2_lds");
         if (config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) return small;
