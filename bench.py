@@ -175,16 +175,25 @@ def main():
                      "kernel_ms": round(kernel_ms, 5)},
     }
     if not args.no_also:
+        # the other measured workloads: the 4096^3 product of the metric, the
+        # ragged single product and the HBM-bound batched TN product (whose
+        # roofline is bytes, not FLOPs)
         also = []
-        for name in ("nn_f16_4096",):
+        for name in ("nn_f16_4096", "nn_f16_ragged_4095x5000x3000", "tn_f16_batched_32x2048x2048x128"):
             if name == w.name:
                 continue
             wa = WORKLOADS[name]
             ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup)
-            also.append({"workload": name, "value": round(wa.flops / (ms_a * 1e-3) / 1e12, 2),
-                         "kernel_tflops": round(wa.flops / (kms_a * 1e-3) / 1e12, 2),
-                         "frac": round(wa.flops / (kms_a * 1e-3) / 1e12 / PEAK_TFLOPS[wa.in_dtype], 4),
-                         "ms_per_step": round(ms_a, 5), "tile_config": cfg_a})
+            entry = {"workload": name, "value": round(wa.flops / (ms_a * 1e-3) / 1e12, 2),
+                     "kernel_tflops": round(wa.flops / (kms_a * 1e-3) / 1e12, 2),
+                     "frac": round(wa.flops / (kms_a * 1e-3) / 1e12 / PEAK_TFLOPS[wa.in_dtype], 4),
+                     "ms_per_step": round(ms_a, 5), "kernel_ms": round(kms_a, 5), "tile_config": cfg_a}
+            es = 4 if wa.out_dtype == "f32" else 2
+            nbytes = (2 * (wa.M * wa.K + wa.K * wa.N) + es * wa.M * wa.N) * max(1, wa.batch)
+            if wa.flops / nbytes < PEAK_TFLOPS[wa.in_dtype] / HBM_GBPS * 1e3:
+                entry["hbm_gbps"] = round(nbytes / (kms_a * 1e-3) / 1e9, 1)
+                entry["hbm_frac"] = round(nbytes / (kms_a * 1e-3) / 1e9 / HBM_GBPS, 4)
+            also.append(entry)
         line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

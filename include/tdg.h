@@ -47,13 +47,14 @@
 #ifndef TDG_H
 #define TDG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define TDG_ABI_VERSION 1
+#define TDG_ABI_VERSION 2
 
 typedef enum { TDG_F16 = 0, TDG_BF16 = 1, TDG_F32 = 2 } tdg_dtype;
 
@@ -109,6 +110,42 @@ tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K,
                        void *C, int64_t ldc, int64_t strideC,
                        int64_t batch,
                        tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream);
+
+/* Split-K calls.  The NineToothed primer (s4) keeps K as a loop inside one
+ * program and names the alternative, splitting K over programs, together
+ * with its cost: a merge step.  tdg_gemm_ws is tdg_gemm_ex with the
+ * library's own choice of configuration plus a caller-owned workspace that
+ * enables a split-K schedule: when the output tiles do not fill whole rounds
+ * of the device's compute units (e.g. 320 tiles on 256 CUs), or there are
+ * few tiles with a long K, the tiles of the last partial round are each cut
+ * into K slices run by separate workgroups; each slice writes an fp32
+ * partial tile into the workspace and the last slice to finish adds them in
+ * slice order and writes C.  The result is the same sum with another
+ * rounding order (bitwise equal for exactly representable sums), and it is
+ * deterministic: the same call on the same device gives the same bits.
+ *
+ * workspace: device memory, 256-byte aligned, at least
+ *   tdg_gemm_workspace_size(...) bytes for these sizes, zero-filled before its
+ *   first use and not written by the caller afterwards (each call leaves
+ *   behind what the next call needs: its counters back at zero).  NULL
+ *   (with workspace_bytes 0) runs without split-K.  Calls that may overlap in
+ *   time (other streams, other threads) must not share a workspace.
+ * Errors: as tdg_gemm_ex, plus TDG_INVALID_VALUE for a misaligned or too
+ * small workspace.
+ * The library still allocates nothing; the caller owns the workspace. */
+tdg_status tdg_gemm_ws(int transb, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, int64_t strideA,
+                       const void *B, int64_t ldb, int64_t strideB,
+                       void *C, int64_t ldc, int64_t strideC,
+                       int64_t batch,
+                       tdg_dtype ab_type, tdg_dtype c_type,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes tdg_gemm_ws needs for these sizes on a device with
+ * `num_cus` compute units (0: the current device); 0 when no split-K
+ * schedule would be used.  An upper bound: operands that cannot take the
+ * vectorised kernels need none. */
+size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus);
 
 /* Number of tile configurations and the name of configuration `config`
  * (e.g. "256x256x64_w2x2_vec"); NULL for an index out of range. */

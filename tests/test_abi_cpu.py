@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(tdg):
 
 
 def test_version_configs_and_status_strings(tdg):
-    assert tdg.tdg_abi_version() == 1
+    assert tdg.tdg_abi_version() == 2
     n = tdg.tdg_num_configs()
     assert n >= 2
     names = [tdg.tdg_config_name(i) for i in range(n)]
@@ -120,7 +120,7 @@ def test_config_selection(tdg):
     assert sel(0, 8192, 8192, 8192) == "256x256x64_s2_w2x4_m16"
     assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 2048, 2048, 128, batch=32) == "256x256x64_s2_w2x4_m16"
-    assert sel(0, 1024, 1024, 1024) == "128x128x64_s2_w2x2_lds"
+    assert sel(0, 1024, 1024, 1024) == "128x128x64_s4_w2x4_m16"
     assert sel(0, 65, 97, 130).endswith("_pred")            # K not a multiple of 8
     assert not sel(1, 64, 97, 128).endswith("_pred")        # TN: N may be ragged
     assert sel(0, 64, 97, 128).endswith("_pred")            # NN: B rows need N % 8 == 0
@@ -134,3 +134,24 @@ def test_no_device_is_reported_not_run(tdg):
         pytest.skip("a GPU is present")
     st = tdg.tdg_gemm_nn(64, 64, 64, P, 64, P, 64, P, 64, 0, 0, None)
     assert st == tdg.TDG_NOT_SUPPORTED
+
+
+def test_split_k_workspace_plan(tdg):
+    """Workspace sizes of the split-K schedule on a 256-CU device.  Problems
+    below one round of 256 x 256 tiles run on 128 x 128 tiles; when those are
+    fewer than 256 they are split into at most 256 / tiles K slices of at
+    least 16 K tiles, if that gives 128 work items or more.  4 bytes per fp32
+    partial element, after a fixed block of one counter per CU (1 KiB)."""
+    tile = 128 * 128 * 4
+    ws = lambda transb, M, N, K, batch=1: tdg.tdg_gemm_workspace_size(transb, M, N, K, batch, 256)
+    assert ws(0, 8192, 8192, 8192) == 0                        # 1024 tiles of 256 x 256
+    assert ws(1, 2048, 2048, 128, 32) == 0                     # 2048 tiles
+    assert ws(0, 4095, 5000, 3000) == 0                        # 320 tiles: cut, not split
+    assert ws(0, 2048, 2048, 8192) == 0                        # 256 tiles of 128 x 128
+    assert ws(0, 1024, 1024, 16384) == 64 * 4 * tile + 1024    # 64 tiles, 4 slices of 64 K tiles
+    assert ws(0, 1024, 1024, 1024) == 0                        # 16 K tiles: too short to split
+    assert ws(0, 300, 520, 16384) == 15 * 16 * tile + 1024     # 15 tiles, 16 slices of 16 K tiles
+    assert ws(0, 300, 520, 8192) == 0                          # 15 x 8 slices: too few work items
+    assert ws(1, 512, 256, 16384) == 8 * 16 * tile + 1024      # 8 tiles, 16 slices
+    assert ws(0, 1024, 1024, 512) == 0
+    assert ws(0, 0, 8, 8) == 0 and ws(0, 8, 8, 0) == 0 and ws(2, 64, 64, 64) == 0

@@ -251,3 +251,92 @@ def test_fp16_subnormal_inputs(tdg):
     c = gpu_gemm(tdg, a, b, "nn", "f32")
     ref = ref_gemm(a, b, "f16", "nn")
     check_exact(c, ref, "f32", "subnormal")
+
+
+# ---------------------------------------------------------------------------
+# Split-K schedule (tdg_gemm_ws)
+# ---------------------------------------------------------------------------
+
+# Problems with few 128 x 128 tiles and a long K: the library cuts every tile
+# into K slices of 16 K tiles (15 tiles x 16 slices, 9 x 16, 8 x 16 on 256
+# CUs); the slices of one tile land on different XCDs.
+SPLIT_SHAPES = [("nn", 300, 520, 16384, "f16", "f32"),
+                ("tn", 257, 264, 16384, "bf16", "bf16"),
+                ("nn", 512, 256, 16384, "bf16", "f16")]
+
+
+def _ws_size(tdg, layout, M, N, K, batch=1):
+    return tdg.tdg_gemm_workspace_size(1 if layout == "tn" else 0, M, N, K, batch, 0)
+
+
+@pytest.mark.parametrize("layout,M,N,K,in_dtype,out_dtype", SPLIT_SHAPES)
+def test_split_k_integer_exact_and_matches_unsplit(tdg, layout, M, N, K, in_dtype, out_dtype):
+    announce("split-k ints", layout, M, N, K, in_dtype, out_dtype)
+    assert _ws_size(tdg, layout, M, N, K) > 0, "shape should take the split-K schedule"
+    a, b = make_inputs(M, N, K, layout, in_dtype, "ints", seed=M + N + K)
+    c = gpu_gemm(tdg, a, b, layout, out_dtype)
+    check_exact(c, ref_gemm(a, b, in_dtype, layout), out_dtype, "split-k %dx%dx%d" % (M, N, K))
+    c0 = tdg.gemm(a.cuda(), b.cuda(), layout=layout, out_dtype=OUT_TORCH[out_dtype], split_k=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c0.cpu())
+
+
+@pytest.mark.parametrize("layout,M,N,K,in_dtype,out_dtype", SPLIT_SHAPES)
+def test_split_k_random_tolerance_and_determinism(tdg, layout, M, N, K, in_dtype, out_dtype):
+    announce("split-k random", layout, M, N, K, in_dtype, out_dtype)
+    a, b = make_inputs(M, N, K, layout, in_dtype, "normal", seed=M * 3 + K)
+    ad, bd = a.cuda(), b.cuda()
+    c1 = tdg.gemm(ad, bd, layout=layout, out_dtype=OUT_TORCH[out_dtype])
+    c2 = tdg.gemm(ad, bd, layout=layout, out_dtype=OUT_TORCH[out_dtype])
+    torch.cuda.synchronize()
+    check_tol(c1.cpu(), ref_gemm(a, b, in_dtype, layout), out_dtype, K, "split-k random")
+    assert torch.equal(c1.view(torch.int16) if c1.element_size() == 2 else c1.view(torch.int32),
+                       c2.view(torch.int16) if c2.element_size() == 2 else c2.view(torch.int32))
+
+
+def test_split_k_workspace_reuse_and_errors(tdg):
+    """One caller-owned workspace serves consecutive calls of different
+    sizes (its counters are back at zero after each call); a workspace that
+    is too small or misaligned is rejected before anything runs."""
+    announce("split-k workspace")
+    shapes = [("nn", 300, 520, 16384), ("nn", 1024, 1024, 16384), ("nn", 512, 256, 16384)]
+    need = max(_ws_size(tdg, *s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for (layout, M, N, K) in shapes + shapes[:1]:
+        a, b = make_inputs(M, N, K, layout, "f16", "ints", seed=K)
+        ad, bd = a.cuda(), b.cuda()
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        st = tdg.tdg_gemm_ws(0, M, N, K, ad.data_ptr(), K, 0, bd.data_ptr(), N, 0, c.data_ptr(), N, 0, 1,
+                             tdg.TDG_F16, tdg.TDG_F32, ws.data_ptr(), need, stream)
+        assert st == tdg.TDG_SUCCESS, tdg.tdg_last_error()
+        torch.cuda.synchronize()
+        rows = sample_rows(M)
+        check_exact(c.cpu()[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f32", "reuse %dx%dx%d" % (M, N, K))
+    M, N, K = 300, 520, 16384
+    a = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    small = _ws_size(tdg, "nn", M, N, K) - 1024
+    st = tdg.tdg_gemm_ws(0, M, N, K, a.data_ptr(), K, 0, b.data_ptr(), N, 0, c.data_ptr(), N, 0, 1,
+                         tdg.TDG_F16, tdg.TDG_F32, ws.data_ptr(), small, stream)
+    assert st == tdg.TDG_INVALID_VALUE and "workspace" in tdg.tdg_last_error()
+    st = tdg.tdg_gemm_ws(0, M, N, K, a.data_ptr(), K, 0, b.data_ptr(), N, 0, c.data_ptr(), N, 0, 1,
+                         tdg.TDG_F16, tdg.TDG_F32, ws.data_ptr() + 16, need - 16, stream)
+    assert st == tdg.TDG_INVALID_VALUE and "aligned" in tdg.tdg_last_error()
+
+
+@pytest.mark.parametrize("layout,M,N,K", [("nn", 4096, 5020, 264),    # 16 x 20 tiles: columns 0..4095 whole rounds
+                                          ("tn", 5000, 4096, 256),    # 20 x 16 tiles: rows 0..4095 whole rounds
+                                          ("tn", 4095, 5000, 3000)])
+def test_partial_round_cut_exact(tdg, layout, M, N, K):
+    """A single problem with a partial last round of 256 x 256 tiles is cut
+    into whole rounds of 256 x 256 tiles and a 128 x 128 remainder (two
+    launches): integer inputs must come out exact on both sides of the cut."""
+    announce("cut", layout, M, N, K)
+    a, b = make_inputs(M, N, K, layout, "f16", "ints", seed=M + 2 * N + K)
+    c = gpu_gemm(tdg, a, b, layout, "f16")
+    rows = sample_rows(M)
+    check_exact(c[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f16", "cut %dx%dx%d" % (M, N, K))
+    cf = gpu_gemm(tdg, a, b, layout, "f32")
+    check_exact(cf[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f32", "cut fp32 %dx%dx%d" % (M, N, K))

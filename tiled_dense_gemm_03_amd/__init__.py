@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     tdg_gemm_nn_batched,
     tdg_gemm_tn,
     tdg_gemm_tn_batched,
+    tdg_gemm_workspace_size,
+    tdg_gemm_ws,
     tdg_last_error,
     tdg_num_configs,
     tdg_select_config,

@@ -24,6 +24,7 @@ lib = ctypes.CDLL(LIB_PATH)
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _int = ctypes.c_int
+_sz = ctypes.c_size_t
 
 _SIG = {
     "tdg_gemm_nn": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
@@ -34,6 +35,9 @@ _SIG = {
                                    _int, _int, _vp]),
     "tdg_gemm_ex": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                            _int, _int, _int, _vp]),
+    "tdg_gemm_ws": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
+                           _int, _int, _vp, _sz, _vp]),
+    "tdg_gemm_workspace_size": (_sz, [_int, _i64, _i64, _i64, _i64, _int]),
     "tdg_num_configs": (_int, []),
     "tdg_config_name": (ctypes.c_char_p, [_int]),
     "tdg_select_config": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int]),
@@ -74,6 +78,16 @@ def tdg_gemm_ex(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strid
                 config, stream):
     return lib.tdg_gemm_ex(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type,
                            c_type, config, stream)
+
+
+def tdg_gemm_ws(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type,
+                workspace, workspace_bytes, stream):
+    return lib.tdg_gemm_ws(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type,
+                           c_type, workspace, workspace_bytes, stream)
+
+
+def tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus):
+    return lib.tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus)
 
 
 def tdg_num_configs():

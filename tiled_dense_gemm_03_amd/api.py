@@ -63,7 +63,22 @@ def select_config(a, b, layout="nn", out_dtype=None):
                                 None, N, batch, _AB[a.dtype], ct)
 
 
-def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1):
+# Split-K workspaces, one per (device, stream) so that calls that may run at
+# the same time never share one; zero-filled once by torch, kept zero-filled by
+# the library.  Replaced by a larger one when a call needs more.
+_workspaces = {}
+
+
+def _workspace(device, stream, nbytes):
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
     """C = A @ B (layout "nn", b is (K, N)) or A @ B^T ("tn", b is (N, K)).
 
     a: (M, K) or (batch, M, K); b likewise batched or not (a 2-D b is shared
@@ -71,7 +86,9 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1):
     fp32 accumulation; out_dtype defaults to the input dtype and may be
     float32.  ``out`` (row-major, unit last stride) is written in place;
     otherwise a new contiguous tensor is returned.  ``config`` forces a tile
-    configuration (tests and sweeps); -1 lets the library choose.
+    configuration (tests and sweeps); -1 lets the library choose, and then
+    ``split_k`` lets it use its split-K schedule (a workspace per device and
+    stream, allocated by torch once).
     """
     _row_major(a, "a")
     _row_major(b, "b")
@@ -97,10 +114,21 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1):
     sA = a.stride(0) if a.dim() == 3 else 0
     sB = b.stride(0) if b.dim() == 3 else 0
     sC = out.stride(0) if out.dim() == 3 else 0
+    transb = 1 if layout == "tn" else 0
     stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        _check(_b.tdg_gemm_ex(1 if layout == "tn" else 0, M, N, K,
-                              a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
-                              out.data_ptr(), _ld(out), sC, batch,
-                              _AB[a.dtype], _CT[odt], int(config), stream))
+        if config == -1 and split_k:
+            need = _b.tdg_gemm_workspace_size(transb, M, N, K, batch, 0)
+            ws = _workspace(a.device, stream, need) if need else None
+            _check(_b.tdg_gemm_ws(transb, M, N, K,
+                                  a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
+                                  out.data_ptr(), _ld(out), sC, batch,
+                                  _AB[a.dtype], _CT[odt],
+                                  ws.data_ptr() if ws is not None else None,
+                                  ws.numel() if ws is not None else 0, stream))
+        else:
+            _check(_b.tdg_gemm_ex(transb, M, N, K,
+                                  a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
+                                  out.data_ptr(), _ld(out), sC, batch,
+                                  _AB[a.dtype], _CT[odt], int(config), stream))
     return out

@@ -15,6 +15,15 @@ struct GemmArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int tiles_per_batch;
+    // Split-K schedule of the 16x16x32 kernel (ignored by the others):
+    // workgroups [0, dp_tiles) each own one whole tile; the remaining
+    // workgroups are sk_split K slices of each of the last tiles.  ws holds
+    // one fp32 partial tile per slice, ws_flags one arrival counter per
+    // split tile (zero between calls).
+    float *ws;
+    int *ws_flags;
+    int dp_tiles;
+    int sk_split;
 };
 
 }  // namespace tdg
@@ -37,4 +46,7 @@ struct GemmArgs {
     X(7, 0, 64, 64, 64, 2, 2, 2, true, "64x64x64_w2x2_vec")                  \
     X(8, 0, 64, 64, 64, 2, 2, 2, false, "64x64x64_w2x2_pred")                \
     X(9, 0, 128, 128, 64, 2, 2, 2, false, "128x128x64_w2x2_pred")           \
-    X(10, 2, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16")
+    X(10, 2, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16")          \
+    X(11, 2, 128, 128, 64, 4, 2, 2, true, "128x128x64_s4_w2x2_m16")          \
+    X(12, 2, 128, 128, 64, 4, 2, 4, true, "128x128x64_s4_w2x4_m16")          \
+    X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")

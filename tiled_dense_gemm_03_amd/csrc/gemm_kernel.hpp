@@ -93,19 +93,19 @@ __device__ __forceinline__ void store_out(void *C, int64_t off, float v) {
     }
 }
 
-// Map the workgroup id to (problem, tile row, tile column).
-//  * Workgroups are handed to the 8 XCDs round-robin (id % 8); renumbering
-//    id -> (id % 8) * share + id / 8 makes each XCD walk a contiguous range of
-//    logical tiles, so tiles that share A rows or B columns meet in the same
-//    XCD's L2.  The renumbering is a bijection for any grid size.
-//  * Logical tiles are ordered in groups of GROUP_M tile rows, column by
-//    column inside a group, so a burst of concurrent tiles covers a compact
-//    block of the output.
-__device__ __forceinline__ void tile_coords(const GemmArgs &p, int &batch, int &tm, int &tn) {
-    const int w = blockIdx.x;
-    const int num = gridDim.x;
+// Workgroups are handed to the 8 XCDs round-robin (id % 8); renumbering
+// id -> (id % 8) * share + id / 8 makes each XCD walk a contiguous range of
+// the `num` logical work items, so tiles that share A rows or B columns meet
+// in the same XCD's L2.  A bijection on [0, num) for any num.
+__device__ __forceinline__ int xcd_order(int w, int num) {
     const int q = num >> 3, r = num & 7, x = w & 7;
-    const int logical = x * q + (x < r ? x : r) + (w >> 3);
+    return x * q + (x < r ? x : r) + (w >> 3);
+}
+
+// Logical tile index -> (problem, tile row, tile column).  Tiles are ordered
+// in groups of GROUP_M tile rows, column by column inside a group, so a burst
+// of concurrent tiles covers a compact block of the output.
+__device__ __forceinline__ void tile_of(const GemmArgs &p, int logical, int &batch, int &tm, int &tn) {
     batch = logical / p.tiles_per_batch;
     const int t = logical - batch * p.tiles_per_batch;
     const int group_size = GROUP_M * p.tiles_n;
@@ -116,6 +116,12 @@ __device__ __forceinline__ void tile_coords(const GemmArgs &p, int &batch, int &
     const int in_group = t - g * group_size;
     tm = first_m + in_group % gm;
     tn = in_group / gm;
+}
+
+// Map the workgroup id to (problem, tile row, tile column): one tile per
+// workgroup, XCD-aware order over the whole grid.
+__device__ __forceinline__ void tile_coords(const GemmArgs &p, int &batch, int &tm, int &tn) {
+    tile_of(p, xcd_order(blockIdx.x, gridDim.x), batch, tm, tn);
 }
 
 // BM x BN workgroup tile, WM x WN waves, each wave owning a

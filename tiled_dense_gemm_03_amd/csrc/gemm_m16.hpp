@@ -97,16 +97,41 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
 
     __shared__ u32x4 smem[STAGES * STAGE];
+    __shared__ int sk_last;
     auto stage_ptr = [&](auto tag) -> u32x4 * { return smem + decltype(tag)::value * STAGE; };
 
-    int batch, tm, tn;
-    tile_coords(p, batch, tm, tn);
+    // ---- work item: a whole tile, or one K slice of a split tile ----
+    // Workgroups [0, dp_tiles) take the first dp_tiles tiles; the rest take
+    // K slices of the remaining tiles, sk_split consecutive work items per
+    // tile.  Each phase is spread over the XCDs on its own, so both the whole
+    // tiles and the slices are balanced over the chip, and the slices of one
+    // tile meet on one XCD.
+    const int nk_all = (p.K + BK - 1) / BK;
+    int batch, tm, tn, kt_begin = 0, kt_end = nk_all, slice = 0, split_tile = -1;
+    {
+        const int w = blockIdx.x, dp = p.dp_tiles;
+        int logical;
+        if (w < dp) {
+            logical = xcd_order(w, dp);
+        } else {
+            const int u = xcd_order(w - dp, (int)gridDim.x - dp);
+            split_tile = u / p.sk_split;
+            slice = u - split_tile * p.sk_split;
+            logical = dp + split_tile;
+            kt_begin = (int)((int64_t)nk_all * slice / p.sk_split);
+            kt_end = (int)((int64_t)nk_all * (slice + 1) / p.sk_split);
+        }
+        tile_of(p, logical, batch, tm, tn);
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_m = wave / WN, wave_n = wave % WN;
-    const int M = p.M, N = p.N, K = p.K;
+    const int M = p.M, N = p.N;
+    // loads stop at the end of this work item's K range (the prefetches past
+    // it read nothing)
+    const int K = p.K < kt_end * BK ? p.K : kt_end * BK;
     const int m0 = tm * BM, n0 = tn * BN;
     const int64_t lda = p.lda, ldb = p.ldb;
 
@@ -222,11 +247,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < RN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = (K + BK - 1) / BK;
     u32x4 af[2][RM], bf[2][RN];
 
-    if (nk > 0) {
-        static_for<0, STAGES>([&](auto s) { issue_to(decltype(s)::value, stage_ptr(s)); });
+    if (kt_end > kt_begin) {
+        static_for<0, STAGES>([&](auto s) { issue_to(kt_begin + decltype(s)::value, stage_ptr(s)); });
         wait_vm_lgkm0<(STAGES - 1) * NDMA>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -239,7 +263,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // of stage s_cur.  The stage is a run-time index (one loop body, no
     // per-stage copies of the code).
     int s_cur = 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
         const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
         u32x4 *cur = smem + s_cur * STAGE;
         u32x4 *nxt = smem + s_nxt * STAGE;
@@ -267,6 +291,68 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         s_cur = s_nxt;
     }
     __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- split tiles: combine the K slices ----
+    // Every slice stores its fp32 partial tile (each lane its own 16-byte
+    // pieces, so each wave store is 1 KiB contiguous) and takes a ticket from
+    // the tile's counter; the slice that draws the last ticket sums the
+    // partials in slice order (the same rounding whichever slice arrives
+    // last), resets the counter for the next call and writes the tile.  No
+    // workgroup ever waits for another.  The partials are written and read
+    // with the device-coherent cache policy (sc1, the policy hipcc itself
+    // gives agent-scope atomic loads and stores on gfx950), the stores have
+    // completed (s_waitcnt) before the ticket is taken, and the ticket is an
+    // agent-scope atomic, so no cache-wide write-back or invalidate is
+    // needed.
+    if (split_tile >= 0) {
+        constexpr int CPOL = 16;                           // sc1
+        const int S = p.sk_split;
+        constexpr int PER_WAVE = RM * RN * 64;             // 16-byte pieces per wave and slice
+        const __amdgpu_buffer_rsrc_t rws =
+            make_rsrc(reinterpret_cast<const char *>(p.ws) + (int64_t)split_tile * S * NW * PER_WAVE * 16);
+        const uint32_t wave_off = (uint32_t)(wave * PER_WAVE + lane) * 16u;
+        const uint32_t mine = (uint32_t)(slice * NW * PER_WAVE) * 16u + wave_off;
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rws,
+                                                       mine + (uint32_t)((i * RN + j) * 64 * 16), 0, CPOL);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);                     // this wave's partial has landed
+        __syncthreads();                                   // ... and every wave's
+        if (tid == 0)
+            sk_last = __hip_atomic_fetch_add(p.ws_flags + split_tile, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (!sk_last) return;
+        // Sum slice by slice, CH accumulators at a time, so that CH loads are
+        // in flight per wait.
+        constexpr int NACC = RM * RN, CH = 8;
+        static_assert(NACC % CH == 0, "accumulator chunks");
+        const uint32_t sstride = (uint32_t)(NW * PER_WAVE) * 16u;
+        static_for<0, NACC / CH>([&](auto chunk) {
+            constexpr int c0 = decltype(chunk)::value * CH;
+            f32x4 sum[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                sum[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rws, wave_off + (uint32_t)((c0 + c) * 64 * 16), 0, CPOL));
+            for (int sl = 1; sl < S; ++sl) {
+                f32x4 t[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c)
+                    t[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rws, sl * sstride + wave_off + (uint32_t)((c0 + c) * 64 * 16),
+                                                         0, CPOL));
+#pragma unroll
+                for (int c = 0; c < CH; ++c) sum[c] += t[c];
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) acc[(c0 + c) / RN][(c0 + c) % RN] = sum[c];
+        });
+        if (tid == 0) __hip_atomic_store(p.ws_flags + split_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- epilogue: fp32 -> output type, store mask of the primer's s5 ----
     // Lane l holds C[m][n] for m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.

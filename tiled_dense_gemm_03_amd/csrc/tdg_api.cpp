@@ -57,11 +57,12 @@ tdg_status fail(tdg_status st, const char *fmt, ...) {
     return st;
 }
 
-// Architecture check, once per device.
+// Architecture check and compute-unit count, once per device.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];          // compute units (valid once g_arch_state is set)
 
-tdg_status check_device() {
+tdg_status check_device(int *cus = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(TDG_NOT_SUPPORTED, "no HIP device is current");
     if (dev < 0 || dev >= kMaxDevices) return fail(TDG_NOT_SUPPORTED, "device index %d out of range", dev);
@@ -71,11 +72,13 @@ tdg_status check_device() {
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return fail(TDG_NOT_SUPPORTED, "cannot query device %d", dev);
         st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         g_arch_state[dev].store(st, std::memory_order_release);
         if (st != 1) return fail(TDG_NOT_SUPPORTED, "device %d is %s, this library targets gfx950", dev,
                                  prop.gcnArchName);
     }
     if (st != 1) return fail(TDG_NOT_SUPPORTED, "device %d is not gfx950", dev);
+    if (cus) *cus = g_cus[dev].load(std::memory_order_relaxed);
     return TDG_SUCCESS;
 }
 
@@ -118,18 +121,70 @@ int config_by_name(const char *name) {
     return -1;
 }
 
-// Tile-configuration choice (measured on MI355X): 256 x 256 tiles on the
-// 16 x 16 x 32 MFMA kernel when the problem has at least one tile per CU
-// (256); 128 x 128 tiles for smaller problems; the register-staged kernel
-// when the direct-load kernels cannot address the operands; the predicated
-// kernel for misaligned operands.
+// Split-K schedule for the 16x16x32 kernel (NineToothed primer s4 names the
+// alternative to keeping K inside one program: split it, at the price of a
+// merge step).  With `cus` workgroups running at once, a problem of fewer
+// tiles than that would leave most of the chip idle; each tile is cut
+// instead into `split` K slices (at most cus / tiles, each at least
+// kMinSliceTiles K tiles), run by separate workgroups and merged by the last
+// slice to finish.  (The kernel also takes whole tiles before the split ones;
+// for a partial last round the merge traffic costs more than it saves, and
+// the cut into 256 x 256 and 128 x 128 parts below serves that case.)
+constexpr int64_t kMinSliceTiles = 16;
+
+struct SplitPlan {
+    int64_t dp_tiles;   // whole tiles, one workgroup each
+    int64_t sk_tiles;   // split tiles
+    int split;          // K slices per split tile (1: no split)
+};
+
+SplitPlan plan_split(int64_t tiles, int64_t nk, int64_t cus) {
+    SplitPlan pl{tiles, 0, 1};
+    if (cus <= 0 || tiles <= 0 || tiles >= cus) return pl;
+    const int64_t rem = tiles % cus;
+    if (rem == 0) return pl;
+    int64_t sp = cus / rem;
+    if (sp > nk / kMinSliceTiles) sp = nk / kMinSliceTiles;
+    if (sp < 2) return pl;
+    pl.dp_tiles = tiles - rem;
+    pl.sk_tiles = rem;
+    pl.split = (int)sp;
+    return pl;
+}
+
+// Workspace layout: one int counter per possible split tile (fewer than
+// `cus` of them) at the start, padded to 256 bytes, then the fp32 partial
+// tiles (split x sk_tiles of them).  The counters sit at the same place
+// whatever the sizes of the call, so the zeros one call leaves behind are
+// where the next call looks for them.
+size_t split_flag_bytes(int64_t cus) { return ((size_t)cus * 4 + 255) / 256 * 256; }
+size_t split_ws_bytes(const Config &cf, const SplitPlan &pl, int64_t cus) {
+    if (pl.split < 2) return 0;
+    return split_flag_bytes(cus) + (size_t)pl.sk_tiles * pl.split * cf.bm * cf.bn * 4;
+}
+
+// Whether a split schedule is worth taking for a problem below one round of
+// 256 x 256 tiles: it must give at least half the chip a work item.
+bool split_pays(const SplitPlan &pl, int64_t cus) {
+    return pl.split >= 2 && pl.sk_tiles * pl.split * 2 >= cus;
+}
+
+// Tile-configuration choice (measured on MI355X), with `cus` the device's
+// compute units: 256 x 256 tiles on the 16 x 16 x 32 MFMA kernel when the
+// problem has at least one such tile per CU; 128 x 128 tiles on the same
+// kernel (8 waves, 4 stages) for smaller problems; the 32 x 32 x 16 direct
+// load kernel or the register-staged kernel when the 16 x 16 x 32 kernel
+// cannot address the operands; the predicated kernel for misaligned
+// operands.
 int choose(int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb, int64_t ldc,
-           int c_type) {
+           int c_type, int64_t cus) {
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
-        if (tiles256 >= 256 && config_ok(kConfigs[id], transb, vec, lda, ldb, ldc, c_type)) return id;
+        if (tiles256 >= cus && config_ok(kConfigs[id], transb, vec, lda, ldb, ldc, c_type)) return id;
+        const int mid = config_by_name("128x128x64_s4_w2x4_m16");
+        if (config_ok(kConfigs[mid], transb, vec, lda, ldb, ldc, c_type)) return mid;
         const int small = config_by_name("128x128x64_s2_w2x2_lds");
         if (config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) return small;
         return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_vec" : "64x64x64_w2x2_vec");
@@ -168,25 +223,11 @@ tdg_status validate(int transb, int64_t M, int64_t N, int64_t K, const void *A, 
     return TDG_SUCCESS;
 }
 
-tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
-               const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
-               tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream) {
-    g_err[0] = '\0';
-    tdg_status st = validate(transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type);
-    if (st != TDG_SUCCESS) return st;
-    if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
-    const bool vec = vec_ok(transb, N, K, A, lda, sA, B, ldb, sB, batch);
-    if (config < -1 || config >= kNumConfigs)
-        return fail(TDG_INVALID_VALUE, "config %d out of range [-1, %d)", config, kNumConfigs);
-    if (config == -1) config = choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type);
+// One launch of configuration `config` over a whole (sub-)problem.
+tdg_status launch(int config, int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
+                  const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
+                  tdg_dtype ab_type, tdg_dtype c_type, void *stream, void *ws, size_t ws_bytes, int cus) {
     const Config &cf = kConfigs[config];
-    if (cf.vec && !vec)
-        return fail(TDG_INVALID_VALUE, "config %s needs 16-byte aligned operands with 8-element granules", cf.name);
-    if (!config_ok(cf, transb, vec, lda, ldb, ldc, c_type))
-        return fail(TDG_INVALID_VALUE, "config %s cannot serve these leading dimensions or this layout", cf.name);
-    st = check_device();
-    if (st != TDG_SUCCESS) return st;
-
     GemmArgs a;
     a.A = static_cast<const uint16_t *>(A);
     a.B = static_cast<const uint16_t *>(B);
@@ -199,7 +240,21 @@ tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64
     a.tiles_m = (int)cdiv(M, cf.bm);
     a.tiles_n = (int)cdiv(N, cf.bn);
     a.tiles_per_batch = a.tiles_m * a.tiles_n;
-    const int64_t grid = (int64_t)a.tiles_per_batch * batch;
+    const int64_t tiles = (int64_t)a.tiles_per_batch * batch;
+    SplitPlan pl{tiles, 0, 1};
+    if (cf.kind == 2 && ws != nullptr) {
+        pl = plan_split(tiles, cdiv(K, cf.bk), cus);
+        if (!split_pays(pl, cus)) pl = SplitPlan{tiles, 0, 1};
+    }
+    const size_t need = split_ws_bytes(cf, pl, cus);
+    if (need > ws_bytes)
+        return fail(TDG_INVALID_VALUE, "workspace of %zu bytes is smaller than the %zu bytes this call needs", ws_bytes,
+                    need);
+    a.ws_flags = need ? static_cast<int *>(ws) : nullptr;
+    a.ws = need ? reinterpret_cast<float *>(static_cast<char *>(ws) + split_flag_bytes(cus)) : nullptr;
+    a.dp_tiles = (int)pl.dp_tiles;
+    a.sk_split = pl.split;
+    const int64_t grid = pl.dp_tiles + pl.sk_tiles * pl.split;
     if (grid > (int64_t)INT_MAX) return fail(TDG_INVALID_VALUE, "too many output tiles");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -210,6 +265,106 @@ tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64
         e = (ab_type == TDG_F16) ? launch_t1_ab0(config, c_type, a, grid, s) : launch_t1_ab1(config, c_type, a, grid, s);
     if (e != hipSuccess) return fail(TDG_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
     return TDG_SUCCESS;
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// Wave quantisation without a merge step: when a single problem has more
+// 256 x 256 tiles than `cus` but not a whole number of rounds, the output is
+// cut into a part that holds whole rounds of 256 x 256 tiles (a band of tile
+// columns, or of tile rows) and the rest, which is covered by 128 x 128
+// tiles, four times as many work items for the same area.  Cost model in
+// units of one 256 x 256 tile's time: a 128 x 128 tile takes 0.4 of it
+// (a quarter of the work at a lower rate).  Returns the cut (a multiple of
+// 256, in columns if *cols else in rows) or 0 when cutting does not pay.
+int64_t plan_retile(int64_t M, int64_t N, int64_t cus, bool *cols) {
+    const int64_t tm = cdiv(M, 256), tn = cdiv(N, 256), tiles = tm * tn;
+    if (cus <= 0 || tiles <= cus || tiles % cus == 0) return 0;
+    double best = (double)cdiv(tiles, cus) * 0.9;
+    int64_t cut = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int64_t mine = pass == 0 ? tm : tn, other = pass == 0 ? tn : tm;
+        const int64_t step = cus / gcd64(mine, cus);          // tile lines per whole round
+        const int64_t lines = (other - 1) / step * step;      // keep a remainder
+        if (lines <= 0) continue;
+        const int64_t rest = pass == 0 ? cdiv(M, 128) * cdiv(N - 256 * lines, 128)
+                                       : cdiv(M - 256 * lines, 128) * cdiv(N, 128);
+        double rem_cost = 0.4 * (double)rest / (double)cus;
+        if (rem_cost < 0.4) rem_cost = 0.4;
+        const double cost = (double)(mine * lines / cus) + rem_cost;
+        if (cost < best) {
+            best = cost;
+            cut = 256 * lines;
+            *cols = pass == 0;
+        }
+    }
+    return cut;
+}
+
+tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
+               const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
+               tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream, void *ws = nullptr,
+               size_t ws_bytes = 0) {
+    g_err[0] = '\0';
+    tdg_status st = validate(transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type);
+    if (st != TDG_SUCCESS) return st;
+    if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
+    const bool vec = vec_ok(transb, N, K, A, lda, sA, B, ldb, sB, batch);
+    if (config < -1 || config >= kNumConfigs)
+        return fail(TDG_INVALID_VALUE, "config %d out of range [-1, %d)", config, kNumConfigs);
+    if (ws != nullptr && ((uintptr_t)ws & 255u))
+        return fail(TDG_INVALID_VALUE, "workspace must be 256-byte aligned");
+    const bool automatic = config == -1;
+    if (!automatic) {
+        const Config &forced = kConfigs[config];
+        if (forced.vec && !vec)
+            return fail(TDG_INVALID_VALUE, "config %s needs 16-byte aligned operands with 8-element granules",
+                        forced.name);
+        if (!config_ok(forced, transb, vec, lda, ldb, ldc, c_type))
+            return fail(TDG_INVALID_VALUE, "config %s cannot serve these leading dimensions or this layout",
+                        forced.name);
+    }
+    int cus = 0;
+    st = check_device(&cus);
+    if (st != TDG_SUCCESS) return st;
+    if (automatic) config = choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    const Config &cf = kConfigs[config];
+
+    // Automatic choice on a single problem with a partial last round of
+    // 256 x 256 tiles: whole rounds on one band of C, 128 x 128 tiles on the
+    // rest (two launches on the stream, disjoint parts of C).
+    if (automatic && cf.kind == 2 && batch == 1) {
+        const int small = config_by_name("128x128x64_s4_w2x4_m16");
+        bool cols = true;
+        const int64_t cut = plan_retile(M, N, cus, &cols);
+        if (cut > 0 && config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) {
+            const int64_t es = (c_type == TDG_F32) ? 4 : 2;
+            const uint16_t *b16 = static_cast<const uint16_t *>(B);
+            const uint16_t *a16 = static_cast<const uint16_t *>(A);
+            char *c8 = static_cast<char *>(C);
+            if (cols) {
+                st = launch(config, transb, M, cut, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, stream,
+                            nullptr, 0, cus);
+                if (st != TDG_SUCCESS) return st;
+                return launch(small, transb, M, N - cut, K, A, lda, 0, transb ? b16 + cut * ldb : b16 + cut, ldb, 0,
+                              c8 + cut * es, ldc, 0, 1, ab_type, c_type, stream, nullptr, 0, cus);
+            }
+            st = launch(config, transb, cut, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, stream,
+                        nullptr, 0, cus);
+            if (st != TDG_SUCCESS) return st;
+            return launch(small, transb, M - cut, N, K, a16 + cut * lda, lda, 0, B, ldb, 0, c8 + cut * ldc * es, ldc,
+                          0, 1, ab_type, c_type, stream, nullptr, 0, cus);
+        }
+    }
+    return launch(config, transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type, stream, ws,
+                  ws_bytes, cus);
 }
 
 }  // namespace
@@ -243,6 +398,28 @@ tdg_status tdg_gemm_tn_batched(int64_t M, int64_t N, int64_t K, const void *A, i
                     stream);
 }
 
+tdg_status tdg_gemm_ws(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
+                       const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
+                       int64_t batch, tdg_dtype ab_type, tdg_dtype c_type, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    return tdg::run(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
+                    stream, workspace, workspace_bytes);
+}
+
+size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus) {
+    if (M <= 0 || N <= 0 || K <= 0 || batch <= 0 || (transb != 0 && transb != 1)) return 0;
+    int cus = num_cus;
+    if (cus <= 0 && tdg::check_device(&cus) != TDG_SUCCESS) return 0;
+    // the configuration the library picks for vectorisable operands
+    const int id = tdg::choose(transb, true, M, N, batch, transb ? K : K, transb ? K : N, N, TDG_F32, cus);
+    const tdg::Config &cf = tdg::kConfigs[id];
+    if (cf.kind != 2) return 0;
+    const int64_t tiles = tdg::cdiv(M, cf.bm) * tdg::cdiv(N, cf.bn) * batch;
+    const tdg::SplitPlan pl = tdg::plan_split(tiles, tdg::cdiv(K, cf.bk), cus);
+    if (!tdg::split_pays(pl, cus)) return 0;
+    return tdg::split_ws_bytes(cf, pl, cus);
+}
+
 tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
                        const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
                        int64_t batch, tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream) {
@@ -266,7 +443,10 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K, const void *A
                       ab_type, c_type, false) != TDG_SUCCESS)
         return -1;
     const bool vec = tdg::vec_ok(transb, N, K, A, lda, 0, B, ldb, 0, batch);
-    return tdg::choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type);
+    int cus = 256;   // the MI355X count when no device is current
+    if (tdg::check_device(&cus) != TDG_SUCCESS) cus = 256;
+    tdg::g_err[0] = '\0';
+    return tdg::choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
 }
 
 const char *tdg_status_string(tdg_status status) {
