@@ -108,6 +108,44 @@ def cpu_baseline(w, seconds_min=10.0):
                          "*batch" if w.batch else "")}
 
 
+def amd_smi_state():
+    """GFX clock (mean over the XCDs), hotspot temperature and socket power of
+    GPU 0 from amd-smi, or None when it cannot be read."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "-p", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        temp = g["temperature"].get("hotspot")
+        power = g["power"].get("socket_power")
+        return {"gfx_clock_mhz": round(sum(clks) / len(clks)) if clks else None,
+                "hotspot_c": temp.get("value") if isinstance(temp, dict) else None,
+                "socket_power_w": power.get("value") if isinstance(power, dict) else None}
+    except Exception:   # no amd-smi, no permission, other output format
+        return None
+
+
+def gpu_state_under_load(tdg, torch, w, kernel_ms, seconds=1.5):
+    """amd-smi sampled while the GPU runs back-to-back launches of the
+    workload (about `seconds` of them, queued before the sample is taken)."""
+    from workloads import TORCH_DTYPE, workload_inputs
+    a, b = workload_inputs(w)
+    a, b = a.cuda(), b.cuda()
+    c = tdg.gemm(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
+    n = max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
+    for _ in range(n):
+        tdg.gemm(a, b, layout=w.layout, out=c)
+    time.sleep(min(0.5, seconds / 3))
+    state = amd_smi_state()
+    torch.cuda.synchronize()
+    if state is not None:
+        state["sampled"] = "amd-smi during %d back-to-back launches of %s" % (n, w.name)
+    return state
+
+
 def calibrate_copy(torch, nbytes=1 << 30, reps=3):
     """A plain copy kernel of known size, for scaling the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE): each dispatch of the elementwise multiply-by-one
@@ -128,6 +166,7 @@ def main():
     ap.add_argument("--workload", default="nn_bf16_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--no-gpu-state", action="store_true", help="skip the amd-smi clock/temperature sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -195,6 +234,8 @@ def main():
                 entry["hbm_frac"] = round(nbytes / (kms_a * 1e-3) / 1e9 / HBM_GBPS, 4)
             also.append(entry)
         line["also"] = also
+    if not args.no_gpu_state:
+        line["gpu_state"] = gpu_state_under_load(tdg, torch, w, kernel_ms)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -340,3 +340,27 @@ def test_partial_round_cut_exact(tdg, layout, M, N, K):
     check_exact(c[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f16", "cut %dx%dx%d" % (M, N, K))
     cf = gpu_gemm(tdg, a, b, layout, "f32")
     check_exact(cf[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f32", "cut fp32 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_output_ownership_map(tdg, layout):
+    """Every output element is written exactly once, by the lane that owns
+    it: with A = identity (M = K) the product is B itself, and B's entries
+    encode their own (row, column) (exact integers in fp16), so a misplaced,
+    missing or doubled element shows up as a wrong code.  Run on every
+    vectorised configuration, over a shape that spans several tiles and
+    ragged edges."""
+    M = K = 520
+    N = 392
+    announce("ownership", layout)
+    code = (torch.arange(M).view(M, 1) % 64) * 32 + (torch.arange(N).view(1, N) % 32) - 1024   # |code| <= 1024
+    a = torch.eye(M, K, dtype=torch.float16)
+    b = code.to(torch.float16)                    # B[k][j] = code(k, j)
+    if layout == "tn":
+        b = b.t().contiguous()                    # stored N x K
+    expect = code.to(torch.float32)
+    for cfg in _config_ids(tdg, True):
+        c = gpu_gemm(tdg, a, b, layout, "f32", config=cfg)
+        bad = (c != expect).nonzero()
+        assert bad.numel() == 0, "%s: %d misplaced elements, first at %s" % (
+            tdg.tdg_config_name(cfg), bad.shape[0], bad[:4].tolist())
