@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TDG_ABI_VERSION 2
+#define TDG_ABI_VERSION 3
 
 typedef enum { TDG_F16 = 0, TDG_BF16 = 1, TDG_F32 = 2 } tdg_dtype;
 
@@ -141,10 +141,36 @@ tdg_status tdg_gemm_ws(int transb, int64_t M, int64_t N, int64_t K,
                        tdg_dtype ab_type, tdg_dtype c_type,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* The general call: any storage order of A, B and C.  The Croqtile
+ * tutorial, chapter 4, gives the contraction layout variants (row.row,
+ * row.col: which operands are stored K-contiguous) and a transposed store of
+ * the accumulator tile (mma.store.transp, for a consumer that wants the other
+ * major order); this call offers all of them:
+ *   transa 0: A stored M x K (lda >= K);  1: A stored K x M (lda >= M).
+ *   transb 0: B stored K x N (ldb >= N);  1: B stored N x K (ldb >= K).
+ *   transc 0: C stored M x N (ldc >= N);  1: C stored N x M (ldc >= M), i.e.
+ *             element (i, j) of the product at C[j * ldc + i].
+ * C[i,j] = sum_{p<K} A(i,p) * B(p,j) as everywhere else; strides, dtypes,
+ * workspace and errors as tdg_gemm_ws (strideC must keep the stored C
+ * matrices disjoint).  A transposed store is the exchanged product
+ * C^T = B^T A^T, run by the same kernels.  Layouts that need an A stored
+ * K x M (transa 1 with transc 0, or transb 0 with transc 1) run on the
+ * vectorised kernel only: 16-byte aligned A and B, leading dimensions, batch
+ * strides and contiguous extents multiples of 8 elements; other operands
+ * return TDG_NOT_SUPPORTED. */
+tdg_status tdg_gemm(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda, int64_t strideA,
+                    const void *B, int64_t ldb, int64_t strideB,
+                    void *C, int64_t ldc, int64_t strideC,
+                    int64_t batch,
+                    tdg_dtype ab_type, tdg_dtype c_type,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes tdg_gemm_ws needs for these sizes on a device with
  * `num_cus` compute units (0: the current device); 0 when no split-K
  * schedule would be used.  An upper bound: operands that cannot take the
- * vectorised kernels need none. */
+ * vectorised kernels need none.  Also valid for tdg_gemm with any
+ * transa, transb, transc (the tile counts do not depend on them). */
 size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus);
 
 /* Number of tile configurations and the name of configuration `config`

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(tdg):
 
 
 def test_version_configs_and_status_strings(tdg):
-    assert tdg.tdg_abi_version() == 2
+    assert tdg.tdg_abi_version() == 3
     n = tdg.tdg_num_configs()
     assert n >= 2
     names = [tdg.tdg_config_name(i) for i in range(n)]

@@ -364,3 +364,71 @@ def test_output_ownership_map(tdg, layout):
         bad = (c != expect).nonzero()
         assert bad.numel() == 0, "%s: %d misplaced elements, first at %s" % (
             tdg.tdg_config_name(cfg), bad.shape[0], bad[:4].tolist())
+
+
+# ---------------------------------------------------------------------------
+# Storage orders: A stored M x K or K x M, B stored K x N or N x K, C stored
+# M x N or N x M (tdg_gemm; the Python front passes transposed views)
+# ---------------------------------------------------------------------------
+
+def _stored(t, transposed):
+    """`t` on the device, as itself or as the transposed view of its
+    transposed copy (same logical matrix, the other major order)."""
+    return t.t().contiguous().cuda().t() if transposed else t.contiguous().cuda()
+
+
+@pytest.mark.parametrize("ta", [0, 1])
+@pytest.mark.parametrize("tb", [0, 1])
+@pytest.mark.parametrize("tc", [0, 1])
+def test_storage_orders_integer_exact(tdg, ta, tb, tc):
+    for (M, N, K) in [(264, 392, 520), (520, 136, 264), (64, 128, 72)]:
+        announce("storage", ta, tb, tc, M, N, K)
+        a, b = make_inputs(M, N, K, "nn", "f16", "ints", seed=M + N + K + 4 * ta + 2 * tb + tc)
+        A, B = _stored(a, ta), _stored(b, tb)
+        out = torch.full((N, M), 77.0, device="cuda").t() if tc else torch.full((M, N), 77.0, device="cuda")
+        tdg.gemm(A, B, layout="nn", out=out)
+        torch.cuda.synchronize()
+        check_exact(out.cpu(), ref_gemm(a, b, "f16", "nn"), "f32", "storage %d%d%d %dx%dx%d" % (ta, tb, tc, M, N, K))
+
+
+@pytest.mark.parametrize("ta,tb,tc", [(1, 0, 0), (1, 1, 1), (0, 0, 1)])
+def test_storage_orders_random_batched(tdg, ta, tb, tc):
+    batch, M, N, K = 3, 136, 264, 392
+    announce("storage random", ta, tb, tc)
+    a, b = make_inputs(M, N, K, "nn", "bf16", "normal", seed=11, batch=batch)
+    A = a.transpose(1, 2).contiguous().cuda().transpose(1, 2) if ta else a.cuda()
+    B = b.transpose(1, 2).contiguous().cuda().transpose(1, 2) if tb else b.cuda()
+    out = (torch.empty((batch, N, M), dtype=torch.bfloat16, device="cuda").transpose(1, 2) if tc
+           else torch.empty((batch, M, N), dtype=torch.bfloat16, device="cuda"))
+    tdg.gemm(A, B, layout="nn", out=out)
+    torch.cuda.synchronize()
+    check_tol(out.cpu(), ref_gemm(a, b, "bf16", "nn"), "bf16", K, "storage random")
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 5016, 264), (5000, 4096, 256)])
+def test_storage_a_transposed_partial_round_cut(tdg, M, N, K):
+    """An A stored K x M through the 256 x 256 / 128 x 128 cut (columns, then
+    rows: the row cut moves A's base along its contiguous dimension)."""
+    announce("cut transa", M, N, K)
+    a, b = make_inputs(M, N, K, "nn", "f16", "ints", seed=M + K)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    tdg.gemm(_stored(a, True), b.cuda(), layout="nn", out=out)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    check_exact(out.cpu()[rows], ref_gemm(a, b, "f16", "nn", rows=rows), "f32", "cut transa")
+
+
+def test_storage_order_support_rules(tdg):
+    """A stored K x M needs the vectorised kernel: a ragged M is refused with
+    TDG_NOT_SUPPORTED; a transposed store with B stored N x K is the plain
+    TN product on exchanged operands and takes any shape."""
+    announce("storage rules")
+    M, N, K = 63, 40, 72
+    a, b = make_inputs(M, N, K, "nn", "f16", "ints", seed=5)
+    with pytest.raises(tdg.TdgError) as err:
+        tdg.gemm(_stored(a, True), b.cuda(), layout="nn", out_dtype=torch.float32)
+    assert err.value.status == tdg.TDG_NOT_SUPPORTED
+    out = torch.empty((N, M), dtype=torch.float32, device="cuda").t()
+    tdg.gemm(a.cuda(), _stored(b, True), layout="nn", out=out)        # ta 0, tb 1, tc 1
+    torch.cuda.synchronize()
+    check_exact(out.cpu(), ref_gemm(a, b, "f16", "nn"), "f32", "transc any shape")

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     TDG_SUCCESS,
     tdg_abi_version,
     tdg_config_name,
+    tdg_gemm,
     tdg_gemm_ex,
     tdg_gemm_nn,
     tdg_gemm_nn_batched,

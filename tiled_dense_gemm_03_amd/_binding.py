@@ -38,6 +38,8 @@ _SIG = {
     "tdg_gemm_ws": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                            _int, _int, _vp, _sz, _vp]),
     "tdg_gemm_workspace_size": (_sz, [_int, _i64, _i64, _i64, _i64, _int]),
+    "tdg_gemm": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
+                        _int, _int, _vp, _sz, _vp]),
     "tdg_num_configs": (_int, []),
     "tdg_config_name": (ctypes.c_char_p, [_int]),
     "tdg_select_config": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int]),
@@ -84,6 +86,12 @@ def tdg_gemm_ws(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strid
                 workspace, workspace_bytes, stream):
     return lib.tdg_gemm_ws(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type,
                            c_type, workspace, workspace_bytes, stream)
+
+
+def tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type,
+             c_type, workspace, workspace_bytes, stream):
+    return lib.tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                        ab_type, c_type, workspace, workspace_bytes, stream)
 
 
 def tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus):

@@ -1,7 +1,8 @@
 """Tensor-level front of the C ABI: shape/stride marshalling only.
 
-Accepts row-major torch tensors (unit last stride, any row stride) on a ROCm
-device, reads their sizes, strides and data pointers, and makes exactly one
+Accepts torch tensors on a ROCm device whose matrices are row-major (unit
+last stride) or column-major (unit second-to-last stride, e.g. a ``.t()``
+view), reads their sizes, strides and data pointers, and makes exactly one
 call into ``libtdg.so`` on ``torch.cuda.current_stream()``.  No arithmetic of
 the product happens here.
 """
@@ -24,12 +25,18 @@ def _check(status):
         raise TdgError(status, _b.tdg_last_error())
 
 
-def _row_major(t, name):
+def _storage(t, name):
+    """(transposed, ld): how the (rows x cols) matrices of `t` are stored --
+    row-major with row stride ld, or column-major (the stored matrix is
+    cols x rows with row stride ld)."""
     if t.dim() not in (2, 3):
         raise ValueError("%s must be 2-D or 3-D (batched), got %d-D" % (name, t.dim()))
-    if t.size(-1) > 1 and t.stride(-1) != 1:
-        raise ValueError("%s must have unit stride in its last dimension" % name)
-    return t
+    rows, cols = t.size(-2), t.size(-1)
+    if cols <= 1 or t.stride(-1) == 1:
+        return False, max(t.stride(-2), cols, 1)
+    if rows <= 1 or t.stride(-2) == 1:
+        return True, max(t.stride(-1), rows, 1)
+    raise ValueError("%s must have unit stride in one of its last two dimensions" % name)
 
 
 def config_names():
@@ -82,21 +89,25 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
     """C = A @ B (layout "nn", b is (K, N)) or A @ B^T ("tn", b is (N, K)).
 
     a: (M, K) or (batch, M, K); b likewise batched or not (a 2-D b is shared
-    by every problem of a batched a).  fp16/bf16 inputs of the same dtype,
-    fp32 accumulation; out_dtype defaults to the input dtype and may be
-    float32.  ``out`` (row-major, unit last stride) is written in place;
-    otherwise a new contiguous tensor is returned.  ``config`` forces a tile
-    configuration (tests and sweeps); -1 lets the library choose, and then
-    ``split_k`` lets it use its split-K schedule (a workspace per device and
-    stream, allocated by torch once).
+    by every problem of a batched a).  Each matrix may be row-major or
+    column-major (a transposed view such as ``x.t()``), A, B and ``out``
+    alike.  fp16/bf16 inputs of the same dtype, fp32 accumulation; out_dtype
+    defaults to the input dtype and may be float32.  ``out`` is written in
+    place; otherwise a new row-major tensor is returned.  ``config`` forces a
+    tile configuration (tests and sweeps; row-major A and C only); -1 lets
+    the library choose, and then ``split_k`` lets it use its split-K schedule
+    (a workspace per device and stream, allocated by torch once).
     """
-    _row_major(a, "a")
-    _row_major(b, "b")
     if a.dtype not in _AB or b.dtype != a.dtype:
         raise TypeError("a and b must both be float16 or both bfloat16 (got %s, %s)" % (a.dtype, b.dtype))
     if not (a.is_cuda and b.is_cuda):
         raise ValueError("a and b must be device tensors")
+    ta, lda = _storage(a, "a")
+    b_col, ldb = _storage(b, "b")
     M, N, K = _dims(a, b, layout)
+    # transb: B stored N x K.  "nn" gives b as (K, N): row-major -> K x N;
+    # "tn" gives b as (N, K): row-major -> N x K.  A column-major view flips it.
+    tb = (layout == "tn") != b_col
     batched = a.dim() == 3 or b.dim() == 3
     batch = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
     if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
@@ -107,28 +118,28 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
     shape = (batch, M, N) if batched else (M, N)
     if out is None:
         out = torch.empty(shape, dtype=odt, device=a.device)
-    else:
-        if tuple(out.shape) != shape or out.dtype != odt:
-            raise ValueError("out must be %s of %s, got %s of %s" % (shape, odt, tuple(out.shape), out.dtype))
-        _row_major(out, "out")
+    elif tuple(out.shape) != shape or out.dtype != odt:
+        raise ValueError("out must be %s of %s, got %s of %s" % (shape, odt, tuple(out.shape), out.dtype))
+    tc, ldc = _storage(out, "out")
     sA = a.stride(0) if a.dim() == 3 else 0
     sB = b.stride(0) if b.dim() == 3 else 0
     sC = out.stride(0) if out.dim() == 3 else 0
-    transb = 1 if layout == "tn" else 0
     stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
-        if config == -1 and split_k:
-            need = _b.tdg_gemm_workspace_size(transb, M, N, K, batch, 0)
+        if config == -1:
+            need = _b.tdg_gemm_workspace_size(int(tb), M, N, K, batch, 0) if split_k else 0
             ws = _workspace(a.device, stream, need) if need else None
-            _check(_b.tdg_gemm_ws(transb, M, N, K,
-                                  a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
-                                  out.data_ptr(), _ld(out), sC, batch,
-                                  _AB[a.dtype], _CT[odt],
-                                  ws.data_ptr() if ws is not None else None,
-                                  ws.numel() if ws is not None else 0, stream))
+            _check(_b.tdg_gemm(int(ta), int(tb), int(tc), M, N, K,
+                               a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
+                               out.data_ptr(), ldc, sC, batch,
+                               _AB[a.dtype], _CT[odt],
+                               ws.data_ptr() if ws is not None else None,
+                               ws.numel() if ws is not None else 0, stream))
         else:
-            _check(_b.tdg_gemm_ex(transb, M, N, K,
-                                  a.data_ptr(), _ld(a), sA, b.data_ptr(), _ld(b), sB,
-                                  out.data_ptr(), _ld(out), sC, batch,
+            if ta or tc:
+                raise ValueError("a forced configuration takes row-major a and out")
+            _check(_b.tdg_gemm_ex(int(tb), M, N, K,
+                                  a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
+                                  out.data_ptr(), ldc, sC, batch,
                                   _AB[a.dtype], _CT[odt], int(config), stream))
     return out

@@ -14,14 +14,14 @@
 
 namespace tdg {
 
-template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TB, int CT, bool VEC>
+template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TA, bool TB, int CT, bool VEC>
 static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
     if constexpr (KIND == 1) {
         hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WM, WN, BK, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 2) {
         static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
-        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, CT, VEC>), dim3((unsigned)grid),
@@ -29,16 +29,16 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
     }
 }
 
-template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool VEC>
+template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TA, bool VEC>
 static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     constexpr bool TB = TDG_TRANSB != 0;
-    if constexpr (KIND >= 1 && !TB && BN / 8 < 16) {
-        return hipErrorInvalidValue;   // NN direct-to-LDS kernels need BN >= 128
+    if constexpr ((KIND >= 1 && !TB && BN / 8 < 16) || (TA && (KIND != 2 || BM / 8 < 16))) {
+        return hipErrorInvalidValue;   // an MC operand needs the direct-to-LDS kernels with >= 128-wide rows
     } else {
         switch (ct) {
-        case OUT_F16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_F16, VEC>(a, grid, s); break;
-        case OUT_BF16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_BF16, VEC>(a, grid, s); break;
-        default: launch_one<KIND, BM, BN, BK, ST, WM, WN, TB, OUT_F32, VEC>(a, grid, s); break;
+        case OUT_F16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TA, TB, OUT_F16, VEC>(a, grid, s); break;
+        case OUT_BF16: launch_one<KIND, BM, BN, BK, ST, WM, WN, TA, TB, OUT_BF16, VEC>(a, grid, s); break;
+        default: launch_one<KIND, BM, BN, BK, ST, WM, WN, TA, TB, OUT_F32, VEC>(a, grid, s); break;
         }
         return hipGetLastError();
     }
@@ -48,10 +48,12 @@ static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t
 #define TDG_CAT(a, b) TDG_CAT2(a, b)
 #define TDG_LAUNCHER TDG_CAT(TDG_CAT(launch_t, TDG_TRANSB), TDG_CAT(_ab, TDG_AB))
 
-hipError_t TDG_LAUNCHER(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
+hipError_t TDG_LAUNCHER(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s) {
     switch (cfg) {
-#define TDG_CASE(ID, KIND, BM, BN, BK, ST, WM, WN, VEC, NAME) \
-    case ID: return launch_ct<KIND, BM, BN, BK, ST, WM, WN, VEC>(ct, a, grid, s);
+#define TDG_CASE(ID, KIND, BM, BN, BK, ST, WM, WN, VEC, NAME)                                   \
+    case ID:                                                                                     \
+        return transa ? launch_ct<KIND, BM, BN, BK, ST, WM, WN, true, VEC>(ct, a, grid, s)     \
+                      : launch_ct<KIND, BM, BN, BK, ST, WM, WN, false, VEC>(ct, a, grid, s);
         TDG_CONFIG_LIST(TDG_CASE)
 #undef TDG_CASE
     default: return hipErrorInvalidValue;

@@ -20,6 +20,11 @@
 //    zero fill of out-of-range reads is the primer's s5 masked load.
 //  * K-tail: a granule whose first k is at or past K gets an out-of-range
 //    offset (A and TN-B); NN-B rows past K fall outside the record count.
+//  * Either operand may be stored K-contiguous ("KC": A as M x K, B as N x K)
+//    or K-strided ("MC": A as K x M, B as K x N).  A KC operand goes through
+//    the K-contiguous LDS layout and 16-byte reads, an MC operand through the
+//    transposing layout and reads described below for NN-B; the MFMA
+//    fragments come out the same either way.
 //
 // LDS layouts (16-byte granules of 8 elements):
 //   A, TN-B: [rows][8 granules], granule g of row r at r*8 + (g ^ ((r>>1)&7)).
@@ -75,15 +80,19 @@ __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) 
 
 // BM x BN workgroup tile, WM x WN waves of (BM/WM) x (BN/WN), K tiles of 64
 // in STAGES LDS stages.
-template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSB, int AB, int CT>
+//
+// TRANSA: false = A stored M x K (KC), true = A stored K x M (MC).
+// TRANSB: false = B stored K x N (MC), true = B stored N x K (KC).
+template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
-    constexpr int BK = 64, KS = 2, KG = 8, BNG = BN / GRAN;
+    constexpr int BK = 64, KS = 2, KG = 8, BNG = BN / GRAN, BMG = BM / GRAN;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int RM = WTM / 16, RN = WTN / 16;
     static_assert(RM * 16 == WTM && RN * 16 == WTN, "wave tile must be a multiple of 16");
     static_assert(NW % 2 == 0, "an even number of waves");
-    static_assert(TRANSB || (BNG >= 16 && (BNG & (BNG - 1)) == 0), "NN B rows: a power of two >= 16 granules");
+    static_assert(TRANSB || (BNG >= 16 && (BNG & (BNG - 1)) == 0), "MC B rows: a power of two >= 16 granules");
+    static_assert(!TRANSA || (BMG >= 16 && (BMG & (BMG - 1)) == 0), "MC A rows: a power of two >= 16 granules");
     constexpr int A_SLOTS = BM * KG, B_SLOTS = BN * KG, STAGE = A_SLOTS + B_SLOTS;
     constexpr int NIA = A_SLOTS / 64, NIB = B_SLOTS / 64;
     static_assert(NIA % NW == 0 && NIB % NW == 0, "whole load instructions per wave");
@@ -91,10 +100,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
     static_assert((STAGES - 1) * NDMA < 64, "vmcnt range");
     static_assert(STAGE * 16 * STAGES <= 160 * 1024, "LDS budget");
-    // NN-B load instruction t covers k rows t*RPB .. +RPB-1; its XOR pattern
-    // repeats every NVB instructions of one wave.
-    constexpr int RPB = 64 / BNG;
+    // An MC load instruction t covers k rows t*RP .. +RP-1 (RP = 64 granules
+    // / granules per k row); its XOR pattern repeats every NV instructions of
+    // one wave (NV = 16 / gcd(16, NW * RP)).
+    constexpr int RPB = 64 / BNG, RPA = 64 / BMG;
     constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
+    constexpr int NVA = !TRANSA ? 1 : 16 / ((NW * RPA) % 16 == 0 ? 16 : ((NW * RPA) % 8 == 0 ? 8 : ((NW * RPA) % 4 == 0 ? 4 : ((NW * RPA) % 2 == 0 ? 2 : 1))));
 
     __shared__ u32x4 smem[STAGES * STAGE];
     __shared__ int sk_last;
@@ -135,7 +146,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int64_t lda = p.lda, ldb = p.ldb;
 
-    const uint16_t *Atile = p.A + (int64_t)batch * p.sA + (int64_t)m0 * lda;
+    const uint16_t *Atile = TRANSA ? p.A + (int64_t)batch * p.sA + m0
+                                   : p.A + (int64_t)batch * p.sA + (int64_t)m0 * lda;
     const uint16_t *Btile = TRANSB ? p.B + (int64_t)batch * p.sB + (int64_t)n0 * ldb
                                    : p.B + (int64_t)batch * p.sB + n0;
     const int a_rows = M - m0 < BM ? M - m0 : BM;
@@ -148,9 +160,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // not depend on q (NW is even), so the byte offset is a_lane + q*a_qs.
     const int kc_row = wave * 8 + (lane >> 3);
     const int kc_g = (lane & 7) ^ kx16(kc_row);
-    const uint32_t a_lane = (uint32_t)((kc_row * lda + kc_g * GRAN) * 2);
-    const uint32_t a_qs = (uint32_t)(NW * 8 * lda * 2);
     const int kc_klim = K - kc_g * GRAN;           // granule loaded while k0 < kc_klim
+    uint32_t a_lane[NVA];
+    uint32_t a_qs;
+    if constexpr (!TRANSA) {
+        a_lane[0] = (uint32_t)((kc_row * lda + kc_g * GRAN) * 2);
+        a_qs = (uint32_t)(NW * 8 * lda * 2);
+    } else {
+        // MC A: as MC B below, with M for N
+#pragma unroll
+        for (int v = 0; v < NVA; ++v) {
+            const int kr = RPA * wave + lane / BMG;
+            const int k = RPA * (v * NW) + kr;
+            const int c = (lane % BMG) ^ nx16(k);
+            a_lane[v] = (m0 + c * GRAN < M) ? (uint32_t)((kr * lda + c * GRAN) * 2) : OOB_OFFSET;
+        }
+        a_qs = (uint32_t)(NW * RPA * lda * 2);
+    }
     uint32_t b_lane[NVB];
     uint32_t b_qs;
     if constexpr (TRANSB) {
@@ -174,9 +200,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         const int k0 = kt * BK;
         const uint32_t base = lds_addr_of(sa) + (uint32_t)wave * 1024u;
         if constexpr (q < QA) {
-            const u32x4 rs = rsrc_words_n(Atile + k0, records_of((int64_t)(a_rows - 1) * lda + K - k0));
-            const uint32_t off = (k0 < kc_klim ? a_lane : OOB_OFFSET) + (uint32_t)q * a_qs;
-            dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+            if constexpr (!TRANSA) {
+                const u32x4 rs = rsrc_words_n(Atile + k0, records_of((int64_t)(a_rows - 1) * lda + K - k0));
+                const uint32_t off = (k0 < kc_klim ? a_lane[0] : OOB_OFFSET) + (uint32_t)q * a_qs;
+                dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+            } else {
+                const u32x4 rs = rsrc_words_n(Atile + (int64_t)k0 * lda,
+                                              records_of((int64_t)(K - k0 - 1) * lda + (M - m0)));
+                const uint32_t off = a_lane[q % NVA] + (uint32_t)q * a_qs;
+                dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+            }
         } else {
             constexpr int qb = q - QA;
             if constexpr (TRANSB) {
@@ -216,26 +249,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
             bn_b[j] = ((8 * fg + jr) * BNG + (c ^ (4 * jr + 2 * (fg & 1)))) * 16 + (q4 & 1) * 8;
         }
     }
+    int am_b[TRANSA ? RM : 1];
+    if constexpr (TRANSA) {
+#pragma unroll
+        for (int i = 0; i < RM; ++i) {
+            const int c = (wave_m * WTM + 16 * i + 4 * q4) / GRAN;
+            am_b[i] = ((8 * fg + jr) * BMG + (c ^ (4 * jr + 2 * (fg & 1)))) * 16 + (q4 & 1) * 8;
+        }
+    }
 
+    // LDS reads of an MC operand: two transposing 8-byte reads (k rows
+    // 0..3 and 4..7 of the lane's run) fill one fragment.
+    auto tr_read = [&](const u32x4 *st, int byte_off, u32x4 &frag, auto htag) {
+        constexpr int h = decltype(htag)::value;
+        const char *base = reinterpret_cast<const char *>(st);
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(base + byte_off));
+        const uint64_t w = __builtin_bit_cast(uint64_t, v);
+        frag[2 * h] = (uint32_t)w;
+        frag[2 * h + 1] = (uint32_t)(w >> 32);
+    };
+    constexpr int DA = TRANSA ? 2 * RM : RM;     // LDS reads for the A fragments of one K step
     auto frag_op = [&](auto dtag, const u32x4 *sa, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
         constexpr int d = decltype(dtag)::value;
         const u32x4 *sb = sa + A_SLOTS;
-        if constexpr (d < RM) {
-            af[d] = sa[a_b[ks] + d * 16 * KG];
+        if constexpr (d < DA) {
+            if constexpr (!TRANSA) {
+                af[d] = sa[a_b[ks] + d * 16 * KG];
+            } else {
+                constexpr int i = d / 2, h = d % 2;
+                tr_read(sa, am_b[i] + (32 * ks + 4 * h) * BMG * 16, af[i], std::integral_constant<int, h>{});
+            }
         } else if constexpr (TRANSB) {
-            constexpr int j = d - RM;
+            constexpr int j = d - DA;
             bf[j] = sb[bt_b[ks] + j * 16 * KG];
         } else {
-            constexpr int j = (d - RM) / 2, h = (d - RM) % 2;
-            const char *base = reinterpret_cast<const char *>(sb);
-            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(base + bn_b[j] + (32 * ks + 4 * h) * BNG * 16));
-            const uint64_t w = __builtin_bit_cast(uint64_t, v);
-            bf[j][2 * h] = (uint32_t)w;
-            bf[j][2 * h + 1] = (uint32_t)(w >> 32);
+            constexpr int j = (d - DA) / 2, h = (d - DA) % 2;
+            tr_read(sb, bn_b[j] + (32 * ks + 4 * h) * BNG * 16, bf[j], std::integral_constant<int, h>{});
         }
     };
-    constexpr int NDS = RM + (TRANSB ? RN : 2 * RN);
+    constexpr int NDS = DA + (TRANSB ? RN : 2 * RN);
     constexpr int NMF = RM * RN;
     auto frags_from = [&](const u32x4 *sa, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
         static_for<0, NDS>([&](auto d) { frag_op(d, sa, ks, af, bf); });

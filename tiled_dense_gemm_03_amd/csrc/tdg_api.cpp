@@ -13,16 +13,17 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "../../include/tdg.h"
 #include "gemm_common.hpp"
 
 namespace tdg {
 
-hipError_t launch_t0_ab0(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s);
-hipError_t launch_t0_ab1(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s);
-hipError_t launch_t1_ab0(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s);
-hipError_t launch_t1_ab1(int cfg, int ct, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_t0_ab0(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_t0_ab1(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_t1_ab0(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_t1_ab1(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
 
 namespace {
 
@@ -86,32 +87,39 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Whether the vectorised path may serve these operands: 16-byte aligned
 // bases, row strides and batch strides that keep every 8-element granule
-// aligned, and contiguous extents (K for A and TN-B, N for NN-B) that are
-// whole granules.
-bool vec_ok(int transb, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
+// aligned, and contiguous extents (K for an A stored M x K or a B stored
+// N x K, M for an A stored K x M, N for a B stored K x N) that are whole
+// granules.
+bool vec_ok(int transa, int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
             const void *B, int64_t ldb, int64_t sB, int64_t batch) {
     if (!aligned16(A) || !aligned16(B)) return false;
-    if ((lda & 7) || (ldb & 7) || (K & 7)) return false;
-    if (!transb && (N & 7)) return false;
+    if ((lda & 7) || (ldb & 7)) return false;
+    if ((transa ? M : K) & 7) return false;
+    if ((transb ? K : N) & 7) return false;
     if (batch > 1 && ((sA & 7) || (sB & 7))) return false;
     return true;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Whether configuration `cf` can serve the operands: the vectorised kinds
-// need vec_ok; the direct-to-LDS kinds also need every in-tile byte offset
-// below 2^31 (buffer offsets are 32-bit) and, for NN, B rows of at least 16
-// granules in LDS.
-bool config_ok(const Config &cf, int transb, bool vec, int64_t lda, int64_t ldb, int64_t ldc, int c_type) {
+// Whether configuration `cf` can serve the operands: an A stored K x M only
+// on the 16 x 16 x 32 kernel; the vectorised kinds need vec_ok; the
+// direct-to-LDS kinds also need every in-tile byte offset below 2^31 (buffer
+// offsets are 32-bit) and, for an operand stored K-strided (A as K x M, B as
+// K x N), rows of at least 16 granules in LDS.
+bool config_ok(const Config &cf, int transa, int transb, bool vec, int64_t lda, int64_t ldb, int64_t ldc,
+               int c_type) {
+    if (transa && cf.kind != 2) return false;
     if (!cf.vec) return true;
     if (!vec) return false;
     if (cf.kind < 1) return true;
     const int64_t lim = (int64_t)1 << 31;
     const int64_t es = (c_type == TDG_F32) ? 4 : 2;
-    if ((int64_t)cf.bm * lda * 2 >= lim || (int64_t)cf.bm * ldc * es >= lim) return false;
-    if (transb ? (int64_t)cf.bn * ldb * 2 >= lim : (int64_t)cf.bk * ldb * 2 >= lim) return false;
+    if ((int64_t)cf.bm * ldc * es >= lim) return false;
+    if ((transa ? (int64_t)cf.bk : (int64_t)cf.bm) * lda * 2 >= lim) return false;
+    if ((transb ? (int64_t)cf.bn : (int64_t)cf.bk) * ldb * 2 >= lim) return false;
     if (!transb && cf.bn / 8 < 16) return false;
+    if (transa && cf.bm / 8 < 16) return false;
     return true;
 }
 
@@ -176,26 +184,35 @@ bool split_pays(const SplitPlan &pl, int64_t cus) {
 // load kernel or the register-staged kernel when the 16 x 16 x 32 kernel
 // cannot address the operands; the predicated kernel for misaligned
 // operands.
-int choose(int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb, int64_t ldc,
-           int c_type, int64_t cus) {
+// An A stored K x M (transa) has only the 16 x 16 x 32 kernel: -1 when that
+// kernel cannot serve the operands.
+int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb,
+           int64_t ldc, int c_type, int64_t cus) {
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
-        if (tiles256 >= cus && config_ok(kConfigs[id], transb, vec, lda, ldb, ldc, c_type)) return id;
+        if (tiles256 >= cus && config_ok(kConfigs[id], transa, transb, vec, lda, ldb, ldc, c_type)) return id;
         const int mid = config_by_name("128x128x64_s4_w2x4_m16");
-        if (config_ok(kConfigs[mid], transb, vec, lda, ldb, ldc, c_type)) return mid;
+        if (config_ok(kConfigs[mid], transa, transb, vec, lda, ldb, ldc, c_type)) return mid;
+        if (transa) return -1;
         const int small = config_by_name("128x128x64_s2_w2x2_lds");
-        if (config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) return small;
+        if (config_ok(kConfigs[small], transa, transb, vec, lda, ldb, ldc, c_type)) return small;
         return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_vec" : "64x64x64_w2x2_vec");
     }
+    if (transa) return -1;
     return config_by_name((cdiv(M, 128) * cdiv(N, 128) * b >= 256) ? "128x128x64_w2x2_pred" : "64x64x64_w2x2_pred");
 }
 
-tdg_status validate(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
-                    const void *B, int64_t ldb, int64_t sB, const void *C, int64_t ldc, int64_t sC,
-                    int64_t batch, int ab_type, int c_type, bool check_pointers = true) {
+// Argument checks in the caller's terms: A stored M x K (transa 0) or K x M
+// (transa 1), B stored K x N (transb 0) or N x K (transb 1), C stored M x N
+// (transc 0) or N x M (transc 1).
+tdg_status validate(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A,
+                    int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB, const void *C, int64_t ldc,
+                    int64_t sC, int64_t batch, int ab_type, int c_type, bool check_pointers = true) {
+    if (transa != 0 && transa != 1) return fail(TDG_INVALID_VALUE, "transa must be 0 or 1");
     if (transb != 0 && transb != 1) return fail(TDG_INVALID_VALUE, "transb must be 0 or 1");
+    if (transc != 0 && transc != 1) return fail(TDG_INVALID_VALUE, "transc must be 0 or 1");
     if (M < 0 || N < 0 || K < 0 || batch < 0)
         return fail(TDG_INVALID_VALUE, "negative size (M=%lld N=%lld K=%lld batch=%lld)", (long long)M,
                     (long long)N, (long long)K, (long long)batch);
@@ -205,18 +222,20 @@ tdg_status validate(int transb, int64_t M, int64_t N, int64_t K, const void *A, 
         return fail(TDG_INVALID_VALUE, "ab_type must be TDG_F16 or TDG_BF16");
     if (c_type != TDG_F16 && c_type != TDG_BF16 && c_type != TDG_F32)
         return fail(TDG_INVALID_VALUE, "c_type must be TDG_F16, TDG_BF16 or TDG_F32");
-    if (lda < (K > 0 ? K : 1)) return fail(TDG_INVALID_VALUE, "lda (%lld) < K (%lld)", (long long)lda, (long long)K);
-    const int64_t bmin = transb ? K : N;
+    const int64_t amin = transa ? M : K, bmin = transb ? K : N, cmin = transc ? M : N;
+    if (lda < (amin > 0 ? amin : 1))
+        return fail(TDG_INVALID_VALUE, "lda (%lld) < %s (%lld)", (long long)lda, transa ? "M" : "K", (long long)amin);
     if (ldb < (bmin > 0 ? bmin : 1))
         return fail(TDG_INVALID_VALUE, "ldb (%lld) < %s (%lld)", (long long)ldb, transb ? "K" : "N", (long long)bmin);
-    if (ldc < (N > 0 ? N : 1)) return fail(TDG_INVALID_VALUE, "ldc (%lld) < N (%lld)", (long long)ldc, (long long)N);
+    if (ldc < (cmin > 0 ? cmin : 1))
+        return fail(TDG_INVALID_VALUE, "ldc (%lld) < %s (%lld)", (long long)ldc, transc ? "M" : "N", (long long)cmin);
     if (sA < 0 || sB < 0 || sC < 0) return fail(TDG_INVALID_VALUE, "negative batch stride");
     if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
     if (check_pointers && C == nullptr) return fail(TDG_INVALID_VALUE, "C is NULL");
     if (check_pointers && K > 0 && (A == nullptr || B == nullptr)) return fail(TDG_INVALID_VALUE, "A or B is NULL");
     if (check_pointers && ((((uintptr_t)A | (uintptr_t)B) & 1u) || ((uintptr_t)C & (c_type == TDG_F32 ? 3u : 1u))))
         return fail(TDG_INVALID_VALUE, "A, B and C must be aligned to their element size");
-    if (batch > 1 && sC < (M - 1) * ldc + N)
+    if (batch > 1 && sC < (transc ? (N - 1) * ldc + M : (M - 1) * ldc + N))
         return fail(TDG_INVALID_VALUE, "strideC (%lld) lets the C matrices of the batch overlap", (long long)sC);
     const int64_t tiles = cdiv(M, 64) * cdiv(N, 64) * batch;
     if (tiles > (int64_t)INT_MAX) return fail(TDG_INVALID_VALUE, "too many output tiles");
@@ -224,7 +243,8 @@ tdg_status validate(int transb, int64_t M, int64_t N, int64_t K, const void *A, 
 }
 
 // One launch of configuration `config` over a whole (sub-)problem.
-tdg_status launch(int config, int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
+tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                  int64_t sA,
                   const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
                   tdg_dtype ab_type, tdg_dtype c_type, void *stream, void *ws, size_t ws_bytes, int cus) {
     const Config &cf = kConfigs[config];
@@ -260,9 +280,11 @@ tdg_status launch(int config, int transb, int64_t M, int64_t N, int64_t K, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (transb == 0)
-        e = (ab_type == TDG_F16) ? launch_t0_ab0(config, c_type, a, grid, s) : launch_t0_ab1(config, c_type, a, grid, s);
+        e = (ab_type == TDG_F16) ? launch_t0_ab0(config, c_type, transa, a, grid, s)
+                                 : launch_t0_ab1(config, c_type, transa, a, grid, s);
     else
-        e = (ab_type == TDG_F16) ? launch_t1_ab0(config, c_type, a, grid, s) : launch_t1_ab1(config, c_type, a, grid, s);
+        e = (ab_type == TDG_F16) ? launch_t1_ab0(config, c_type, transa, a, grid, s)
+                                 : launch_t1_ab1(config, c_type, transa, a, grid, s);
     if (e != hipSuccess) return fail(TDG_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
     return TDG_SUCCESS;
 }
@@ -308,15 +330,31 @@ int64_t plan_retile(int64_t M, int64_t N, int64_t cus, bool *cols) {
     return cut;
 }
 
-tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t sA,
-               const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
+// C = op(A) * op(B) (A stored M x K or K x M, B stored K x N or N x K),
+// written as C or as C^T.  A transposed store is the product with the
+// operands exchanged, C^T = B^T A^T: (transa, transb, transc = 1) on (A, B)
+// runs as (!transb, !transa, 0) on (B, A) with M and N exchanged.
+tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+               int64_t sA, const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
                tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream, void *ws = nullptr,
                size_t ws_bytes = 0) {
     g_err[0] = '\0';
-    tdg_status st = validate(transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type);
+    tdg_status st = validate(transa, transb, transc, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type,
+                             c_type);
     if (st != TDG_SUCCESS) return st;
     if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
-    const bool vec = vec_ok(transb, N, K, A, lda, sA, B, ldb, sB, batch);
+    const int ta_in = transa, tb_in = transb, tc_in = transc;
+    if (transc) {
+        const int ta = !transb, tb = !transa;
+        transa = ta;
+        transb = tb;
+        transc = 0;
+        std::swap(M, N);
+        std::swap(A, B);
+        std::swap(lda, ldb);
+        std::swap(sA, sB);
+    }
+    const bool vec = vec_ok(transa, transb, M, N, K, A, lda, sA, B, ldb, sB, batch);
     if (config < -1 || config >= kNumConfigs)
         return fail(TDG_INVALID_VALUE, "config %d out of range [-1, %d)", config, kNumConfigs);
     if (ws != nullptr && ((uintptr_t)ws & 255u))
@@ -327,14 +365,19 @@ tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64
         if (forced.vec && !vec)
             return fail(TDG_INVALID_VALUE, "config %s needs 16-byte aligned operands with 8-element granules",
                         forced.name);
-        if (!config_ok(forced, transb, vec, lda, ldb, ldc, c_type))
+        if (!config_ok(forced, transa, transb, vec, lda, ldb, ldc, c_type))
             return fail(TDG_INVALID_VALUE, "config %s cannot serve these leading dimensions or this layout",
                         forced.name);
     }
     int cus = 0;
     st = check_device(&cus);
     if (st != TDG_SUCCESS) return st;
-    if (automatic) config = choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    if (automatic) config = choose(transa, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    if (config < 0)
+        return fail(TDG_NOT_SUPPORTED,
+                    "layout transa=%d transb=%d transc=%d runs on the vectorised kernel only: 16-byte aligned A and B, "
+                    "leading dimensions, batch strides and contiguous extents multiples of 8 elements",
+                    ta_in, tb_in, tc_in);
     const Config &cf = kConfigs[config];
 
     // Automatic choice on a single problem with a partial last round of
@@ -344,27 +387,27 @@ tdg_status run(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64
         const int small = config_by_name("128x128x64_s4_w2x4_m16");
         bool cols = true;
         const int64_t cut = plan_retile(M, N, cus, &cols);
-        if (cut > 0 && config_ok(kConfigs[small], transb, vec, lda, ldb, ldc, c_type)) {
+        if (cut > 0 && config_ok(kConfigs[small], transa, transb, vec, lda, ldb, ldc, c_type)) {
             const int64_t es = (c_type == TDG_F32) ? 4 : 2;
             const uint16_t *b16 = static_cast<const uint16_t *>(B);
             const uint16_t *a16 = static_cast<const uint16_t *>(A);
             char *c8 = static_cast<char *>(C);
             if (cols) {
-                st = launch(config, transb, M, cut, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, stream,
-                            nullptr, 0, cus);
+                st = launch(config, transa, transb, M, cut, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type,
+                            stream, nullptr, 0, cus);
                 if (st != TDG_SUCCESS) return st;
-                return launch(small, transb, M, N - cut, K, A, lda, 0, transb ? b16 + cut * ldb : b16 + cut, ldb, 0,
-                              c8 + cut * es, ldc, 0, 1, ab_type, c_type, stream, nullptr, 0, cus);
+                return launch(small, transa, transb, M, N - cut, K, A, lda, 0, transb ? b16 + cut * ldb : b16 + cut,
+                              ldb, 0, c8 + cut * es, ldc, 0, 1, ab_type, c_type, stream, nullptr, 0, cus);
             }
-            st = launch(config, transb, cut, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, stream,
-                        nullptr, 0, cus);
+            st = launch(config, transa, transb, cut, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type,
+                        stream, nullptr, 0, cus);
             if (st != TDG_SUCCESS) return st;
-            return launch(small, transb, M - cut, N, K, a16 + cut * lda, lda, 0, B, ldb, 0, c8 + cut * ldc * es, ldc,
-                          0, 1, ab_type, c_type, stream, nullptr, 0, cus);
+            return launch(small, transa, transb, M - cut, N, K, transa ? a16 + cut : a16 + cut * lda, lda, 0, B, ldb,
+                          0, c8 + cut * ldc * es, ldc, 0, 1, ab_type, c_type, stream, nullptr, 0, cus);
         }
     }
-    return launch(config, transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type, stream, ws,
-                  ws_bytes, cus);
+    return launch(config, transa, transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type,
+                  stream, ws, ws_bytes, cus);
 }
 
 }  // namespace
@@ -374,19 +417,19 @@ extern "C" {
 
 tdg_status tdg_gemm_nn(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                        void *C, int64_t ldc, tdg_dtype ab_type, tdg_dtype c_type, void *stream) {
-    return tdg::run(0, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, -1, stream);
+    return tdg::run(0, 0, 0, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, -1, stream);
 }
 
 tdg_status tdg_gemm_tn(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                        void *C, int64_t ldc, tdg_dtype ab_type, tdg_dtype c_type, void *stream) {
-    return tdg::run(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, -1, stream);
+    return tdg::run(0, 1, 0, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, ab_type, c_type, -1, stream);
 }
 
 tdg_status tdg_gemm_nn_batched(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
                                const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
                                int64_t strideC, int64_t batch, tdg_dtype ab_type, tdg_dtype c_type,
                                void *stream) {
-    return tdg::run(0, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
+    return tdg::run(0, 0, 0, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
                     stream);
 }
 
@@ -394,7 +437,7 @@ tdg_status tdg_gemm_tn_batched(int64_t M, int64_t N, int64_t K, const void *A, i
                                const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
                                int64_t strideC, int64_t batch, tdg_dtype ab_type, tdg_dtype c_type,
                                void *stream) {
-    return tdg::run(1, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
+    return tdg::run(0, 1, 0, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
                     stream);
 }
 
@@ -402,8 +445,16 @@ tdg_status tdg_gemm_ws(int transb, int64_t M, int64_t N, int64_t K, const void *
                        const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
                        int64_t batch, tdg_dtype ab_type, tdg_dtype c_type, void *workspace, size_t workspace_bytes,
                        void *stream) {
-    return tdg::run(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type, -1,
-                    stream, workspace, workspace_bytes);
+    return tdg::run(0, transb, 0, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type,
+                    -1, stream, workspace, workspace_bytes);
+}
+
+tdg_status tdg_gemm(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                    int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                    int64_t strideC, int64_t batch, tdg_dtype ab_type, tdg_dtype c_type, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return tdg::run(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                    ab_type, c_type, -1, stream, workspace, workspace_bytes);
 }
 
 size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus) {
@@ -411,7 +462,8 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
     int cus = num_cus;
     if (cus <= 0 && tdg::check_device(&cus) != TDG_SUCCESS) return 0;
     // the configuration the library picks for vectorisable operands
-    const int id = tdg::choose(transb, true, M, N, batch, transb ? K : K, transb ? K : N, N, TDG_F32, cus);
+    const int id = tdg::choose(0, transb, true, M, N, batch, K, transb ? K : N, N, TDG_F32, cus);
+    if (id < 0) return 0;
     const tdg::Config &cf = tdg::kConfigs[id];
     if (cf.kind != 2) return 0;
     const int64_t tiles = tdg::cdiv(M, cf.bm) * tdg::cdiv(N, cf.bn) * batch;
@@ -423,7 +475,7 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
 tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
                        const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC,
                        int64_t batch, tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream) {
-    return tdg::run(transb, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type,
+    return tdg::run(0, transb, 0, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type, c_type,
                     config, stream);
 }
 
@@ -439,14 +491,14 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K, const void *A
                       tdg_dtype c_type) {
     // Batch strides play no part in the choice except through alignment; take
     // them as granule multiples here.
-    if (tdg::validate(transb, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, batch > 1 ? (M - 1) * ldc + N : 0, batch,
+    if (tdg::validate(0, transb, 0, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, batch > 1 ? (M - 1) * ldc + N : 0, batch,
                       ab_type, c_type, false) != TDG_SUCCESS)
         return -1;
-    const bool vec = tdg::vec_ok(transb, N, K, A, lda, 0, B, ldb, 0, batch);
+    const bool vec = tdg::vec_ok(0, transb, M, N, K, A, lda, 0, B, ldb, 0, batch);
     int cus = 256;   // the MI355X count when no device is current
     if (tdg::check_device(&cus) != TDG_SUCCESS) cus = 256;
     tdg::g_err[0] = '\0';
-    return tdg::choose(transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    return tdg::choose(0, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
 }
 
 const char *tdg_status_string(tdg_status status) {
