@@ -173,13 +173,38 @@ tdg_status tdg_gemm(int transa, int transb, int transc, int64_t M, int64_t N, in
  * transa, transb, transc (the tile counts do not depend on them). */
 size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus);
 
+/* Autotuning (tile selection by measurement).  Times every tile
+ * configuration that can serve these arguments, and the library's own
+ * schedule, `reps` calls each on the caller's buffers and stream, and records
+ * the fastest for this process: later automatic calls (tdg_gemm*,
+ * tdg_gemm_nn/tn*) on the same device with the same storage orders, sizes,
+ * types, batch and alignment class run that configuration, and
+ * tdg_select_config reports it.  Unlike every other call this one
+ * synchronises `stream` (it waits for its timing events) and writes C
+ * (with the product, many times).  *best_config receives the configuration
+ * index, or -1 when the library's own schedule won.  reps in [1, 1000].
+ * Errors as tdg_gemm, plus TDG_LAUNCH_FAILED when nothing could be timed. */
+tdg_status tdg_autotune(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda, int64_t strideA,
+                        const void *B, int64_t ldb, int64_t strideB,
+                        void *C, int64_t ldc, int64_t strideC,
+                        int64_t batch,
+                        tdg_dtype ab_type, tdg_dtype c_type,
+                        void *workspace, size_t workspace_bytes,
+                        int reps, int *best_config, void *stream);
+
+/* Forget every autotuning result of this process. */
+void tdg_autotune_clear(void);
+
 /* Number of tile configurations and the name of configuration `config`
  * (e.g. "256x256x64_w2x2_vec"); NULL for an index out of range. */
 int tdg_num_configs(void);
 const char *tdg_config_name(int config);
 
 /* The configuration the library would choose for these arguments (pointers
- * are inspected for alignment only, never dereferenced); -1 on bad args. */
+ * are inspected for alignment only, never dereferenced); -1 on bad args.
+ * A problem tuned by tdg_autotune (transa = transc = 0) reports the tuned
+ * configuration. */
 int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K,
                       const void *A, int64_t lda, const void *B, int64_t ldb,
                       const void *C, int64_t ldc, int64_t batch,

@@ -155,3 +155,28 @@ def test_split_k_workspace_plan(tdg):
     assert ws(1, 512, 256, 16384) == 8 * 16 * tile + 1024      # 8 tiles, 16 slices
     assert ws(0, 1024, 1024, 512) == 0
     assert ws(0, 0, 8, 8) == 0 and ws(0, 8, 8, 0) == 0 and ws(2, 64, 64, 64) == 0
+
+
+def test_autotune_argument_checks(tdg):
+    import ctypes
+    best = ctypes.c_int(7)
+    st = tdg.tdg_autotune(0, 0, 0, 64, 64, 64, P, 64, 0, P, 64, 0, P, 64, 0, 1, 0, 0, None, 0, 0, best, None)
+    assert st == tdg.TDG_INVALID_VALUE and "reps" in tdg.tdg_last_error()
+    st = tdg.tdg_autotune(0, 0, 0, 64, 64, 64, P, 32, 0, P, 64, 0, P, 64, 0, 1, 0, 0, None, 0, 5, best, None)
+    assert st == tdg.TDG_INVALID_VALUE and "lda" in tdg.tdg_last_error()
+    import torch
+    if not torch.cuda.is_available():
+        st = tdg.tdg_autotune(0, 0, 0, 64, 64, 64, P, 64, 0, P, 64, 0, P, 64, 0, 1, 0, 0, None, 0, 5, best, None)
+        assert st == tdg.TDG_NOT_SUPPORTED
+    tdg.tdg_autotune_clear()
+
+
+def test_general_entry_point_checks(tdg):
+    """tdg_gemm checks leading dimensions against each storage order."""
+    g = lambda ta, tb, tc, lda, ldb, ldc: tdg.tdg_gemm(ta, tb, tc, 40, 24, 16, P, lda, 0, P, ldb, 0, P, ldc, 0, 1,
+                                                         0, 0, None, 0, None)
+    assert g(1, 0, 0, 32, 24, 24) == tdg.TDG_INVALID_VALUE and "lda" in tdg.tdg_last_error()   # A is K x M: lda >= 40
+    assert g(0, 1, 0, 16, 8, 24) == tdg.TDG_INVALID_VALUE and "ldb" in tdg.tdg_last_error()    # B is N x K: ldb >= 16
+    assert g(0, 0, 1, 16, 24, 24) == tdg.TDG_INVALID_VALUE and "ldc" in tdg.tdg_last_error()   # C is N x M: ldc >= 40
+    assert g(2, 0, 0, 16, 24, 24) == tdg.TDG_INVALID_VALUE
+    assert g(0, 0, 2, 16, 24, 24) == tdg.TDG_INVALID_VALUE

@@ -432,3 +432,45 @@ def test_storage_order_support_rules(tdg):
     tdg.gemm(a.cuda(), _stored(b, True), layout="nn", out=out)        # ta 0, tb 1, tc 1
     torch.cuda.synchronize()
     check_exact(out.cpu(), ref_gemm(a, b, "f16", "nn"), "f32", "transc any shape")
+
+
+# ---------------------------------------------------------------------------
+# Autotuning (tdg_autotune)
+# ---------------------------------------------------------------------------
+
+def test_autotune_records_and_serves_the_winner(tdg):
+    """The tuned configuration serves later automatic calls of the same
+    problem (seen through tdg_select_config) and computes the same exact
+    product; clearing the cache restores the library's own choice."""
+    M, N, K = 1024, 1024, 1024
+    announce("autotune", M, N, K)
+    tdg.tdg_autotune_clear()
+    a, b = make_inputs(M, N, K, "nn", "f16", "ints", seed=21)
+    ad, bd = a.cuda(), b.cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    default = tdg.select_config(ad, bd, out_dtype=torch.float32)
+    name = tdg.autotune(ad, bd, out=out, reps=3)
+    assert name == "auto" or name in tdg.config_names()
+    chosen = tdg.tdg_config_name(tdg.select_config(ad, bd, out_dtype=torch.float32))
+    if name != "auto":
+        assert chosen == name
+    c = tdg.gemm(ad, bd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_exact(c.cpu(), ref_gemm(a, b, "f16", "nn"), "f32", "after autotune")
+    tdg.tdg_autotune_clear()
+    assert tdg.select_config(ad, bd, out_dtype=torch.float32) == default
+
+
+def test_autotune_transposed_operands(tdg):
+    M, N, K = 520, 264, 392
+    announce("autotune storage")
+    a, b = make_inputs(M, N, K, "nn", "bf16", "ints", seed=22)
+    A, B = _stored(a, True), _stored(b, True)
+    out = torch.empty((N, M), dtype=torch.float32, device="cuda").t()
+    name = tdg.autotune(A, B, out=out, reps=2)
+    assert name == "auto" or name in tdg.config_names()
+    out.zero_()
+    tdg.gemm(A, B, out=out)
+    torch.cuda.synchronize()
+    check_exact(out.cpu(), ref_gemm(a, b, "bf16", "nn"), "f32", "autotuned storage")
+    tdg.tdg_autotune_clear()

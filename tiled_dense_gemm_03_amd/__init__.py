@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     TDG_NOT_SUPPORTED,
     TDG_SUCCESS,
     tdg_abi_version,
+    tdg_autotune,
+    tdg_autotune_clear,
     tdg_config_name,
     tdg_gemm,
     tdg_gemm_ex,
@@ -31,4 +33,4 @@ from ._binding import (  # noqa: F401
     tdg_select_config,
     tdg_status_string,
 )
-from .api import TdgError, config_names, gemm, select_config  # noqa: F401
+from .api import TdgError, autotune, config_names, gemm, select_config  # noqa: F401

@@ -40,6 +40,9 @@ _SIG = {
     "tdg_gemm_workspace_size": (_sz, [_int, _i64, _i64, _i64, _i64, _int]),
     "tdg_gemm": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                         _int, _int, _vp, _sz, _vp]),
+    "tdg_autotune": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                            _i64, _int, _int, _vp, _sz, _int, ctypes.POINTER(_int), _vp]),
+    "tdg_autotune_clear": (None, []),
     "tdg_num_configs": (_int, []),
     "tdg_config_name": (ctypes.c_char_p, [_int]),
     "tdg_select_config": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int]),
@@ -96,6 +99,18 @@ def tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, 
 
 def tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus):
     return lib.tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus)
+
+
+def tdg_autotune(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                 ab_type, c_type, workspace, workspace_bytes, reps, best_config, stream):
+    """best_config: a ctypes.c_int (passed by reference)."""
+    return lib.tdg_autotune(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                            batch, ab_type, c_type, workspace, workspace_bytes, reps, ctypes.byref(best_config),
+                            stream)
+
+
+def tdg_autotune_clear():
+    lib.tdg_autotune_clear()
 
 
 def tdg_num_configs():

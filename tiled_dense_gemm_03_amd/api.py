@@ -6,6 +6,8 @@ view), reads their sizes, strides and data pointers, and makes exactly one
 call into ``libtdg.so`` on ``torch.cuda.current_stream()``.  No arithmetic of
 the product happens here.
 """
+import ctypes
+
 import torch
 
 from . import _binding as _b
@@ -85,19 +87,8 @@ def _workspace(device, stream, nbytes):
     return ws
 
 
-def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
-    """C = A @ B (layout "nn", b is (K, N)) or A @ B^T ("tn", b is (N, K)).
-
-    a: (M, K) or (batch, M, K); b likewise batched or not (a 2-D b is shared
-    by every problem of a batched a).  Each matrix may be row-major or
-    column-major (a transposed view such as ``x.t()``), A, B and ``out``
-    alike.  fp16/bf16 inputs of the same dtype, fp32 accumulation; out_dtype
-    defaults to the input dtype and may be float32.  ``out`` is written in
-    place; otherwise a new row-major tensor is returned.  ``config`` forces a
-    tile configuration (tests and sweeps; row-major A and C only); -1 lets
-    the library choose, and then ``split_k`` lets it use its split-K schedule
-    (a workspace per device and stream, allocated by torch once).
-    """
+def _marshal(a, b, layout, out_dtype, out):
+    """Sizes, storage orders, strides and the output tensor of one call."""
     if a.dtype not in _AB or b.dtype != a.dtype:
         raise TypeError("a and b must both be float16 or both bfloat16 (got %s, %s)" % (a.dtype, b.dtype))
     if not (a.is_cuda and b.is_cuda):
@@ -124,12 +115,29 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
     sA = a.stride(0) if a.dim() == 3 else 0
     sB = b.stride(0) if b.dim() == 3 else 0
     sC = out.stride(0) if out.dim() == 3 else 0
+    return (int(ta), int(tb), int(tc), M, N, K, lda, sA, ldb, sB, ldc, sC, batch, odt, out)
+
+
+def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
+    """C = A @ B (layout "nn", b is (K, N)) or A @ B^T ("tn", b is (N, K)).
+
+    a: (M, K) or (batch, M, K); b likewise batched or not (a 2-D b is shared
+    by every problem of a batched a).  Each matrix may be row-major or
+    column-major (a transposed view such as ``x.t()``), A, B and ``out``
+    alike.  fp16/bf16 inputs of the same dtype, fp32 accumulation; out_dtype
+    defaults to the input dtype and may be float32.  ``out`` is written in
+    place; otherwise a new row-major tensor is returned.  ``config`` forces a
+    tile configuration (tests and sweeps; row-major A and C only); -1 lets
+    the library choose, and then ``split_k`` lets it use its split-K schedule
+    (a workspace per device and stream, allocated by torch once).
+    """
+    ta, tb, tc, M, N, K, lda, sA, ldb, sB, ldc, sC, batch, odt, out = _marshal(a, b, layout, out_dtype, out)
     stream = torch.cuda.current_stream(a.device).cuda_stream
     with torch.cuda.device(a.device):
         if config == -1:
-            need = _b.tdg_gemm_workspace_size(int(tb), M, N, K, batch, 0) if split_k else 0
+            need = _b.tdg_gemm_workspace_size(tb, M, N, K, batch, 0) if split_k else 0
             ws = _workspace(a.device, stream, need) if need else None
-            _check(_b.tdg_gemm(int(ta), int(tb), int(tc), M, N, K,
+            _check(_b.tdg_gemm(ta, tb, tc, M, N, K,
                                a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
                                out.data_ptr(), ldc, sC, batch,
                                _AB[a.dtype], _CT[odt],
@@ -138,8 +146,28 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
         else:
             if ta or tc:
                 raise ValueError("a forced configuration takes row-major a and out")
-            _check(_b.tdg_gemm_ex(int(tb), M, N, K,
+            _check(_b.tdg_gemm_ex(tb, M, N, K,
                                   a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
                                   out.data_ptr(), ldc, sC, batch,
                                   _AB[a.dtype], _CT[odt], int(config), stream))
     return out
+
+
+def autotune(a, b, layout="nn", out_dtype=None, out=None, reps=10):
+    """Time every tile configuration (and the library's own schedule) on
+    these operands and remember the fastest for later ``gemm`` calls of the
+    same problem in this process.  Synchronises the current stream and
+    writes ``out``.  Returns the winning configuration's name, or "auto"."""
+    ta, tb, tc, M, N, K, lda, sA, ldb, sB, ldc, sC, batch, odt, out = _marshal(a, b, layout, out_dtype, out)
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    best = ctypes.c_int(-2)
+    with torch.cuda.device(a.device):
+        need = _b.tdg_gemm_workspace_size(tb, M, N, K, batch, 0)
+        ws = _workspace(a.device, stream, need) if need else None
+        _check(_b.tdg_autotune(ta, tb, tc, M, N, K,
+                               a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
+                               out.data_ptr(), ldc, sC, batch,
+                               _AB[a.dtype], _CT[odt],
+                               ws.data_ptr() if ws is not None else None,
+                               ws.numel() if ws is not None else 0, int(reps), best, stream))
+    return "auto" if best.value < 0 else _b.tdg_config_name(best.value)

@@ -12,7 +12,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "../../include/tdg.h"
@@ -63,9 +65,10 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_cus[kMaxDevices];          // compute units (valid once g_arch_state is set)
 
-tdg_status check_device(int *cus = nullptr) {
+tdg_status check_device(int *cus = nullptr, int *device = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(TDG_NOT_SUPPORTED, "no HIP device is current");
+    if (device) *device = dev;
     if (dev < 0 || dev >= kMaxDevices) return fail(TDG_NOT_SUPPORTED, "device index %d out of range", dev);
     int st = g_arch_state[dev].load(std::memory_order_acquire);
     if (st == 0) {
@@ -330,20 +333,45 @@ int64_t plan_retile(int64_t M, int64_t N, int64_t cus, bool *cols) {
     return cut;
 }
 
+// Autotuning results: for a problem (device, storage orders, sizes, types
+// and whether the operands can take the vectorised kernels), the
+// configuration measured fastest by tdg_autotune, or -1 when the automatic
+// schedule won.
+struct TuneKey {
+    int dev, transa, transb, transc, ab, ct, vec;
+    int64_t M, N, K, batch;
+    bool operator<(const TuneKey &o) const {
+        return std::tie(dev, transa, transb, transc, ab, ct, vec, M, N, K, batch) <
+               std::tie(o.dev, o.transa, o.transb, o.transc, o.ab, o.ct, o.vec, o.M, o.N, o.K, o.batch);
+    }
+};
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tune;
+
+// The tuned configuration for `k`, or -2 when the problem was not tuned.
+int tuned_config(const TuneKey &k) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tune.find(k);
+    return it == g_tune.end() ? -2 : it->second;
+}
+
 // C = op(A) * op(B) (A stored M x K or K x M, B stored K x N or N x K),
 // written as C or as C^T.  A transposed store is the product with the
 // operands exchanged, C^T = B^T A^T: (transa, transb, transc = 1) on (A, B)
 // runs as (!transb, !transa, 0) on (B, A) with M and N exchanged.
+// An automatic call (config -1) of a tuned problem takes the tuned
+// configuration (use_tuned false: the library's own choice, for tuning).
 tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                int64_t sA, const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
                tdg_dtype ab_type, tdg_dtype c_type, int config, void *stream, void *ws = nullptr,
-               size_t ws_bytes = 0) {
+               size_t ws_bytes = 0, bool use_tuned = true) {
     g_err[0] = '\0';
     tdg_status st = validate(transa, transb, transc, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type,
                              c_type);
     if (st != TDG_SUCCESS) return st;
     if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
     const int ta_in = transa, tb_in = transb, tc_in = transc;
+    const int64_t M_in = M, N_in = N;
     if (transc) {
         const int ta = !transb, tb = !transa;
         transa = ta;
@@ -369,10 +397,18 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
             return fail(TDG_INVALID_VALUE, "config %s cannot serve these leading dimensions or this layout",
                         forced.name);
     }
-    int cus = 0;
-    st = check_device(&cus);
+    int cus = 0, dev = 0;
+    st = check_device(&cus, &dev);
     if (st != TDG_SUCCESS) return st;
-    if (automatic) config = choose(transa, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    bool tuned = false;
+    if (automatic && use_tuned) {
+        const int t = tuned_config(TuneKey{dev, ta_in, tb_in, tc_in, ab_type, c_type, vec ? 1 : 0, M_in, N_in, K, batch});
+        if (t >= 0 && config_ok(kConfigs[t], transa, transb, vec, lda, ldb, ldc, c_type)) {
+            config = t;
+            tuned = true;
+        }
+    }
+    if (automatic && !tuned) config = choose(transa, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
     if (config < 0)
         return fail(TDG_NOT_SUPPORTED,
                     "layout transa=%d transb=%d transc=%d runs on the vectorised kernel only: 16-byte aligned A and B, "
@@ -383,7 +419,7 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
     // Automatic choice on a single problem with a partial last round of
     // 256 x 256 tiles: whole rounds on one band of C, 128 x 128 tiles on the
     // rest (two launches on the stream, disjoint parts of C).
-    if (automatic && cf.kind == 2 && batch == 1) {
+    if (automatic && !tuned && cf.kind == 2 && batch == 1) {
         const int small = config_by_name("128x128x64_s4_w2x4_m16");
         bool cols = true;
         const int64_t cut = plan_retile(M, N, cus, &cols);
@@ -406,8 +442,9 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
                           0, c8 + cut * ldc * es, ldc, 0, 1, ab_type, c_type, stream, nullptr, 0, cus);
         }
     }
+    // (a tuned configuration runs as it was timed: without split-K)
     return launch(config, transa, transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type, c_type,
-                  stream, ws, ws_bytes, cus);
+                  stream, tuned ? nullptr : ws, tuned ? 0 : ws_bytes, cus);
 }
 
 }  // namespace
@@ -479,6 +516,76 @@ tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K, const void *
                     config, stream);
 }
 
+tdg_status tdg_autotune(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A,
+                        int64_t lda, int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C,
+                        int64_t ldc, int64_t strideC, int64_t batch, tdg_dtype ab_type, tdg_dtype c_type,
+                        void *workspace, size_t workspace_bytes, int reps, int *best_config, void *stream) {
+    using namespace tdg;
+    g_err[0] = '\0';
+    if (reps < 1 || reps > 1000) return fail(TDG_INVALID_VALUE, "reps must be in [1, 1000]");
+    tdg_status st = validate(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                             batch, ab_type, c_type);
+    if (st != TDG_SUCCESS) return st;
+    int cus = 0, dev = 0;
+    st = check_device(&cus, &dev);
+    if (st != TDG_SUCCESS) return st;
+    if (M == 0 || N == 0 || batch == 0 || K == 0) {
+        if (best_config) *best_config = -1;
+        return TDG_SUCCESS;
+    }
+    // the candidates in the library's own terms (a transposed store runs as
+    // the exchanged product)
+    const int ta = transc ? !transb : transa, tb = transc ? !transa : transb;
+    const void *iA = transc ? B : A, *iB = transc ? A : B;
+    const int64_t iM = transc ? N : M, iN = transc ? M : N, ilda = transc ? ldb : lda, ildb = transc ? lda : ldb;
+    const int64_t isA = transc ? strideB : strideA, isB = transc ? strideA : strideB;
+    const bool vec = vec_ok(ta, tb, iM, iN, K, iA, ilda, isA, iB, ildb, isB, batch);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return fail(TDG_LAUNCH_FAILED, "cannot create timing events");
+    }
+    int best = -2;
+    float best_ms = 0.0f;
+    for (int cand = -1; cand < kNumConfigs; ++cand) {
+        if (cand >= 0 && ((kConfigs[cand].vec && !vec) ||
+                          !config_ok(kConfigs[cand], ta, tb, vec, ilda, ildb, ldc, c_type)))
+            continue;
+        auto call = [&]() {
+            return run(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                       ab_type, c_type, cand, stream, cand < 0 ? workspace : nullptr, cand < 0 ? workspace_bytes : 0,
+                       false);
+        };
+        if (call() != TDG_SUCCESS) continue;                 // not servable (e.g. layout limits)
+        if (hipEventRecord(e0, s) != hipSuccess) break;
+        bool ok = true;
+        for (int r = 0; r < reps && ok; ++r) ok = call() == TDG_SUCCESS;
+        if (!ok || hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) break;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) break;
+        if (best == -2 || ms < best_ms) {
+            best = cand;
+            best_ms = ms;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (best == -2) return fail(TDG_LAUNCH_FAILED, "no configuration could be timed: %s", g_err);
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        g_tune[TuneKey{dev, transa, transb, transc, ab_type, c_type, vec ? 1 : 0, M, N, K, batch}] = best;
+    }
+    if (best_config) *best_config = best;
+    g_err[0] = '\0';
+    return TDG_SUCCESS;
+}
+
+void tdg_autotune_clear(void) {
+    std::lock_guard<std::mutex> lock(tdg::g_tune_mu);
+    tdg::g_tune.clear();
+}
+
 int tdg_num_configs(void) { return tdg::kNumConfigs; }
 
 const char *tdg_config_name(int config) {
@@ -495,9 +602,13 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K, const void *A
                       ab_type, c_type, false) != TDG_SUCCESS)
         return -1;
     const bool vec = tdg::vec_ok(0, transb, M, N, K, A, lda, 0, B, ldb, 0, batch);
-    int cus = 256;   // the MI355X count when no device is current
-    if (tdg::check_device(&cus) != TDG_SUCCESS) cus = 256;
+    int cus = 256, dev = -1;   // the MI355X count when no device is current
+    if (tdg::check_device(&cus, &dev) != TDG_SUCCESS) cus = 256, dev = -1;
     tdg::g_err[0] = '\0';
+    if (dev >= 0) {
+        const int t = tdg::tuned_config(tdg::TuneKey{dev, 0, transb, 0, ab_type, c_type, vec ? 1 : 0, M, N, K, batch});
+        if (t >= 0) return t;
+    }
     return tdg::choose(0, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
 }
 
