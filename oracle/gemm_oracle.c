@@ -36,6 +36,14 @@
  *   orc_tile_geometry grid sizes, K-step count and, for one (i, j, p), the
  *                     nominal and valid element ranges of the A tile, B tile
  *                     and output tile ([NT] s3, s4, s5).
+ *   orc_decode_f8     E4M3 / E5M2 bit pattern -> exact double ([CQ] FP8
+ *                     operands; bit layouts from the OCP 8-bit formats).
+ *   orc_decode_e8m0   E8M0 block-scale byte -> 2^(e - 127).
+ *   orc_gemm_f8       the scaled 8-bit TN product: per K block, the block's
+ *                     contraction times the two operands' block scales,
+ *                     summed over blocks, then times the row scales ([CQ]
+ *                     per-tile scaled contraction and the separate scale
+ *                     statement).
  *
  * Build: gcc -O3 -fPIC -shared -pthread -ffp-contract=off (see build.py).
  */
@@ -345,5 +353,169 @@ int orc_tiled_gemm(int transb, int fmt, int64_t M, int64_t N, int64_t K,
         }
     }
     free(acc); free(lhs); free(rhs);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit floating-point operands with scales                                 */
+/* ------------------------------------------------------------------------ */
+
+/* The Croqtile tutorial ch.4 (the variants after the four-step rhythm: FP8
+ * operands with per-tile scaling) names the operand types f8_e4m3 and f8_e5m2
+ * and gives the scaled contraction: the product of an operand pair is
+ * multiplied by the two operands' scales after the contraction, with no
+ * separate dequantisation pass.  The pages do not define the bit layouts;
+ * they are taken here from the OCP 8-bit floating point formats:
+ *   E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits.  No infinities: the
+ *         all-ones exponent is an ordinary binade except for fraction 7,
+ *         which is NaN, so the largest finite value is 1.75 * 2^8 = 448.
+ *   E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits, binary16-like: the
+ *         all-ones exponent is inf (fraction 0) or NaN.
+ * Both have subnormals f * 2^(1 - bias - fraction_bits) at exponent 0.
+ * The block scales are E8M0 (OCP microscaling): 8 exponent bits, no sign and
+ * no fraction, value 2^(e - 127), 0xFF is NaN. */
+enum { ORC_FMT_E4M3 = 4, ORC_FMT_E5M2 = 5 };
+
+double orc_decode_f8(int fmt, uint8_t bits) {
+    const int eb = (fmt == ORC_FMT_E4M3) ? 4 : 5;
+    const int mb = 7 - eb;
+    const int bias = (1 << (eb - 1)) - 1;
+    const int emax_field = (1 << eb) - 1;
+    const int sign = bits >> 7;
+    const int e = (bits >> mb) & emax_field;
+    const int f = bits & ((1 << mb) - 1);
+    double v;
+    if (fmt == ORC_FMT_E4M3 && e == emax_field && f == (1 << mb) - 1) {
+        v = NAN;
+    } else if (fmt == ORC_FMT_E5M2 && e == emax_field) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else if (e == 0) {
+        v = ldexp((double)f, 1 - bias - mb);
+    } else {
+        v = ldexp((double)((1 << mb) + f), e - bias - mb);
+    }
+    return sign ? -v : v;
+}
+
+double orc_decode_e8m0(uint8_t bits) {
+    return bits == 0xFF ? NAN : ldexp(1.0, (int)bits - 127);
+}
+
+void orc_decode_f8_array(int fmt, const uint8_t *bits, double *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_decode_f8(fmt, bits[i]);
+}
+
+void orc_decode_e8m0_array(const uint8_t *bits, double *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_decode_e8m0(bits[i]);
+}
+
+typedef struct {
+    int64_t N, K, block, nblk;
+    const double *Ad, *Bd;     /* decoded A (M x K) and B (N x K), K per row */
+    const double *XA, *XB;     /* decoded block scales, nblk per row (or NULL) */
+    const double *SA, *SB;     /* row scales (or NULL) */
+    double *C;
+    int64_t ldc, r0, r1;
+} f8_job;
+
+static void *f8_worker(void *arg) {
+    const f8_job *jb = (const f8_job *)arg;
+    const int64_t N = jb->N, K = jb->K, blk = jb->block, nb = jb->nblk;
+    for (int64_t i = jb->r0; i < jb->r1; ++i) {
+        const double *a = jb->Ad + i * K;
+        for (int64_t j = 0; j < N; ++j) {
+            const double *b = jb->Bd + j * K;
+            double total = 0.0;
+            for (int64_t t = 0; t < nb; ++t) {
+                /* the contraction over one block of K ... */
+                double part = 0.0;
+                const int64_t k1 = (t + 1) * blk < K ? (t + 1) * blk : K;
+                for (int64_t k = t * blk; k < k1; ++k) part += a[k] * b[k];
+                /* ... then the two operands' scales for that block */
+                if (jb->XA) part *= jb->XA[i * nb + t];
+                if (jb->XB) part *= jb->XB[j * nb + t];
+                total += part;
+            }
+            if (jb->SA) total *= jb->SA[i];
+            if (jb->SB) total *= jb->SB[j];
+            jb->C[i * jb->ldc + j] = total;
+        }
+    }
+    return NULL;
+}
+
+/*
+ * orc_gemm_f8: C[i][j] = sa(i) * sb(j) * sum_t xa(i,t) * xb(j,t) *
+ *                        sum_{k in block t} dec(A[i,k]) * dec(B[j,k])
+ * in binary64, for A M x K (row stride lda, format afmt) and B N x K (row
+ * stride ldb, format bfmt): the TN form C = A * B^T.  Block t covers
+ * k = t*block .. min((t+1)*block, K) - 1.
+ *   xa(i,t) = 2^(XA[i*ldxa + t] - 127) (E8M0), or 1 when XA is NULL; xb alike
+ *             with XB, ldxb.
+ *   sa(i)   = SA[i*inc_sa] (inc_sa 0: one scale for the whole operand), or 1
+ *             when SA is NULL; sb alike.
+ * K == 0 gives zeros.  Threads split the rows of C.
+ */
+int orc_gemm_f8(int64_t M, int64_t N, int64_t K,
+                const uint8_t *A, int64_t lda, int afmt,
+                const uint8_t *B, int64_t ldb, int bfmt,
+                const uint8_t *XA, int64_t ldxa, const uint8_t *XB, int64_t ldxb, int64_t block,
+                const float *SA, int64_t inc_sa, const float *SB, int64_t inc_sb,
+                double *C, int64_t ldc, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || block < 1) return ORC_BAD_ARG;
+    if ((afmt != ORC_FMT_E4M3 && afmt != ORC_FMT_E5M2) || (bfmt != ORC_FMT_E4M3 && bfmt != ORC_FMT_E5M2))
+        return ORC_BAD_ARG;
+    const int64_t nb = cdiv64(K, block);
+    if (lda < K || ldb < K || ldc < N || (XA && ldxa < nb) || (XB && ldxb < nb) || inc_sa < 0 || inc_sb < 0)
+        return ORC_BAD_ARG;
+    if (nthreads < 1) nthreads = 1;
+    if (M == 0 || N == 0) return ORC_OK;
+    double lut_a[256], lut_b[256];
+    for (int v = 0; v < 256; ++v) {
+        lut_a[v] = orc_decode_f8(afmt, (uint8_t)v);
+        lut_b[v] = orc_decode_f8(bfmt, (uint8_t)v);
+    }
+    const size_t kk = (size_t)(K ? K : 1), bb = (size_t)(nb ? nb : 1);
+    double *Ad = (double *)malloc(sizeof(double) * (size_t)M * kk);
+    double *Bd = (double *)malloc(sizeof(double) * (size_t)N * kk);
+    double *xa = XA ? (double *)malloc(sizeof(double) * (size_t)M * bb) : NULL;
+    double *xb = XB ? (double *)malloc(sizeof(double) * (size_t)N * bb) : NULL;
+    double *sa = SA ? (double *)malloc(sizeof(double) * (size_t)M) : NULL;
+    double *sb = SB ? (double *)malloc(sizeof(double) * (size_t)N) : NULL;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    f8_job *jobs = (f8_job *)malloc(sizeof(f8_job) * (size_t)nthreads);
+    if (!Ad || !Bd || (XA && !xa) || (XB && !xb) || (SA && !sa) || (SB && !sb) || !tid || !jobs) {
+        free(Ad); free(Bd); free(xa); free(xb); free(sa); free(sb); free(tid); free(jobs);
+        return ORC_NO_MEM;
+    }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) Ad[i * K + k] = lut_a[A[i * lda + k]];
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k) Bd[j * K + k] = lut_b[B[j * ldb + k]];
+    for (int64_t i = 0; xa && i < M; ++i)
+        for (int64_t t = 0; t < nb; ++t) xa[i * nb + t] = orc_decode_e8m0(XA[i * ldxa + t]);
+    for (int64_t j = 0; xb && j < N; ++j)
+        for (int64_t t = 0; t < nb; ++t) xb[j * nb + t] = orc_decode_e8m0(XB[j * ldxb + t]);
+    for (int64_t i = 0; sa && i < M; ++i) sa[i] = (double)SA[i * inc_sa];
+    for (int64_t j = 0; sb && j < N; ++j) sb[j] = (double)SB[j * inc_sb];
+    int nt = nthreads;
+    if (nt > M) nt = (int)M;
+    for (int t = 0; t < nt; ++t) {
+        f8_job *jb = &jobs[t];
+        jb->N = N; jb->K = K; jb->block = block; jb->nblk = nb;
+        jb->Ad = Ad; jb->Bd = Bd; jb->XA = xa; jb->XB = xb; jb->SA = sa; jb->SB = sb;
+        jb->C = C; jb->ldc = ldc;
+        jb->r0 = M * t / nt;
+        jb->r1 = M * (t + 1) / nt;
+    }
+    int started = 0;
+    for (int t = 1; t < nt; ++t) {
+        if (pthread_create(&tid[t], NULL, f8_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    f8_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
+    for (int t = started + 1; t < nt; ++t) f8_worker(&jobs[t]);
+    free(Ad); free(Bd); free(xa); free(xb); free(sa); free(sb); free(tid); free(jobs);
     return ORC_OK;
 }

@@ -3,13 +3,15 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this module.  It wraps ``liboracle.so`` (plain C, built by
 ``oracle/build.py`` with gcc) through ctypes and works on numpy arrays of raw
-fp16/bf16 bit patterns (``uint16``), so that the oracle consumes exactly the
-bits the GPU consumes.  Nothing here imports the GPU library.
+fp16/bf16 bit patterns (``uint16``) and E4M3/E5M2/E8M0 bytes (``uint8``), so
+that the oracle consumes exactly the bits the GPU consumes.  Nothing here
+imports the GPU library.
 
 What each call computes is documented in ``gemm_oracle.c``; the sources are
 the NineToothed GEMM primer (studypath task3 appendix, s3-s6, s8) for the
 definition, index map, tail masks and accumulator precision, and the Croqtile
-tutorial ch.4 ([N,K] right operand) for the TN form.
+tutorial ch.4 ([N,K] right operand) for the TN form and for the FP8 operands
+with per-tile scales.
 """
 import ctypes
 import os
@@ -20,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 # The oracle's own format codes (see gemm_oracle.c).
-FMT = {"f16": 0, "bf16": 1, "f32": 2, "f64": 3}
+FMT = {"f16": 0, "bf16": 1, "f32": 2, "f64": 3, "e4m3": 4, "e5m2": 5}
 
 _lib = None
 
@@ -52,6 +54,17 @@ def _load():
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, p, i64]
     lib.orc_tile_geometry.restype = ctypes.c_int
     lib.orc_tile_geometry.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, p]
+    lib.orc_decode_f8.restype = ctypes.c_double
+    lib.orc_decode_f8.argtypes = [ctypes.c_int, ctypes.c_uint8]
+    lib.orc_decode_e8m0.restype = ctypes.c_double
+    lib.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
+    lib.orc_decode_f8_array.restype = None
+    lib.orc_decode_f8_array.argtypes = [ctypes.c_int, p, p, i64]
+    lib.orc_decode_e8m0_array.restype = None
+    lib.orc_decode_e8m0_array.argtypes = [p, p, i64]
+    lib.orc_gemm_f8.restype = ctypes.c_int
+    lib.orc_gemm_f8.argtypes = [i64, i64, i64, p, i64, ctypes.c_int, p, i64, ctypes.c_int,
+                                p, i64, p, i64, i64, p, i64, p, i64, p, i64, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -178,3 +191,78 @@ def tile_geometry(M, N, K, BM, BN, BK, i=0, j=0, p=0) -> dict:
         "b_valid": ((r[19], r[20]), (r[21], r[22])),
         "c_valid": ((r[23], r[24]), (r[25], r[26])),
     }
+
+
+def _bytes(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("8-bit oracle inputs are uint8 bit patterns, got %s" % a.dtype)
+    return a
+
+
+def decode_f8(bits, fmt: str) -> np.ndarray:
+    """E4M3 / E5M2 bit patterns (uint8) -> exact float64 values."""
+    b = np.ascontiguousarray(_bytes(bits))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().orc_decode_f8_array(FMT[fmt], _ptr(b), _ptr(out), b.size)
+    return out
+
+
+def decode_e8m0(bits) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(e - 127) (0xFF -> NaN)."""
+    b = np.ascontiguousarray(_bytes(bits))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().orc_decode_e8m0_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def gemm_f8(a_bits, b_bits, a_fmt: str, b_fmt: str, xa=None, xb=None, sa=None, sb=None,
+            block: int = 32, nthreads=None) -> np.ndarray:
+    """Scaled 8-bit TN product in float64 (C = A B^T with scales).
+
+    ``a_bits`` (M, K) and ``b_bits`` (N, K) uint8 patterns of ``a_fmt`` /
+    ``b_fmt`` ("e4m3" | "e5m2").  ``xa`` (M, cdiv(K, block)) and ``xb``
+    (N, cdiv(K, block)) are optional E8M0 block-scale bytes; ``sa`` (M,) or
+    (1,) and ``sb`` (N,) or (1,) are optional float32 row scales (a length-1
+    array is one scale for the whole operand).  Returns float64 (M, N).
+    """
+    a = np.ascontiguousarray(_bytes(a_bits))
+    b = np.ascontiguousarray(_bytes(b_bits))
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("shape mismatch")
+    M, K = a.shape
+    N = b.shape[0]
+    nb = (K + block - 1) // block
+
+    def blk(x, rows):
+        if x is None:
+            return None, 0
+        x = np.ascontiguousarray(_bytes(x))
+        if x.shape != (rows, nb):
+            raise ValueError("block scales must be (%d, %d), got %s" % (rows, nb, x.shape))
+        return x, nb
+
+    def row(x, rows):
+        if x is None:
+            return None, 0
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(-1))
+        if x.size not in (1, rows):
+            raise ValueError("row scales must have 1 or %d entries" % rows)
+        return x, (0 if x.size == 1 else 1)
+
+    xa_, ldxa = blk(xa, M)
+    xb_, ldxb = blk(xb, N)
+    sa_, inca = row(sa, M)
+    sb_, incb = row(sb, N)
+    c = np.zeros((M, N), dtype=np.float64)
+    nt = nthreads or default_threads()
+    keep = (xa_, xb_, sa_, sb_)  # noqa: F841  (alive across the call)
+    rc = _load().orc_gemm_f8(M, N, K, _ptr(a), K, FMT[a_fmt], _ptr(b), K, FMT[b_fmt],
+                             _ptr(xa_) if xa_ is not None else None, ldxa,
+                             _ptr(xb_) if xb_ is not None else None, ldxb, block,
+                             _ptr(sa_) if sa_ is not None else None, inca,
+                             _ptr(sb_) if sb_ is not None else None, incb,
+                             _ptr(c), N, nt)
+    if rc != 0:
+        raise ValueError("orc_gemm_f8 failed with %d" % rc)
+    return c

@@ -23,7 +23,35 @@ int orc_tiled_gemm(int transb, int fmt, int64_t M, int64_t N, int64_t K, const u
                    int drop_last_k, double *C, int64_t ldc);
 int orc_tile_geometry(int64_t M, int64_t N, int64_t K, int64_t BM, int64_t BN, int64_t BK, int64_t i, int64_t j,
                       int64_t p, int64_t *g);
+double orc_decode_f8(int fmt, uint8_t bits);
+double orc_decode_e8m0(uint8_t bits);
+int orc_gemm_f8(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, int afmt, const uint8_t *B,
+                int64_t ldb, int bfmt, const uint8_t *XA, int64_t ldxa, const uint8_t *XB, int64_t ldxb,
+                int64_t block, const float *SA, int64_t inc_sa, const float *SB, int64_t inc_sb, double *C,
+                int64_t ldc, int nthreads);
+static int f8_cases(void) {
+    const int64_t M = 13, N = 11, K = 70, nb = 3;
+    uint8_t *A = malloc(M * K), *B = malloc(N * K), *XA = malloc(M * nb), *XB = malloc(N * nb);
+    float *SA = malloc(sizeof(float) * M), *SB = malloc(sizeof(float) * N);
+    double *C = malloc(sizeof(double) * M * N);
+    for (int v = 0; v < 256; ++v) { orc_decode_f8(4, (uint8_t)v); orc_decode_f8(5, (uint8_t)v); orc_decode_e8m0((uint8_t)v); }
+    for (int64_t i = 0; i < M * K; ++i) A[i] = (uint8_t)((i * 37) & 0x77);
+    for (int64_t i = 0; i < N * K; ++i) B[i] = (uint8_t)((i * 11) & 0x7B);
+    for (int64_t i = 0; i < M * nb; ++i) XA[i] = (uint8_t)(120 + i % 9);
+    for (int64_t i = 0; i < N * nb; ++i) XB[i] = (uint8_t)(125 + i % 5);
+    for (int64_t i = 0; i < M; ++i) SA[i] = 0.5f + (float)i / 16;
+    for (int64_t i = 0; i < N; ++i) SB[i] = 1.5f - (float)i / 32;
+    int bad = 0;
+    bad |= orc_gemm_f8(M, N, K, A, K, 4, B, K, 5, XA, nb, XB, nb, 32, SA, 1, SB, 1, C, N, 3);
+    bad |= orc_gemm_f8(M, N, K, A, K, 5, B, K, 4, NULL, 0, XB, nb, 32, SA, 0, NULL, 0, C, N, 1);
+    bad |= orc_gemm_f8(M, N, 0, A, K, 4, B, K, 4, NULL, 0, NULL, 0, 32, NULL, 0, NULL, 0, C, N, 2);
+    bad |= orc_gemm_f8(M, N, K, A, K, 4, B, K, 4, XA, nb - 1, NULL, 0, 32, NULL, 0, NULL, 0, C, N, 2) == 0;
+    bad |= orc_gemm_f8(M, N, K, A, K, 3, B, K, 4, NULL, 0, NULL, 0, 32, NULL, 0, NULL, 0, C, N, 2) == 0;
+    free(A); free(B); free(XA); free(XB); free(SA); free(SB); free(C);
+    return bad;
+}
 int main(void) {
+    if (f8_cases()) { printf("f8 cases failed\n"); return 9; }
     for (int f = 0; f < 2; ++f)
         for (int v = 0; v < 65536; ++v) {
             double d = orc_decode(f, (uint16_t)v);

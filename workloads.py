@@ -14,6 +14,12 @@ float32 from the stated distribution; convert to the input dtype.
   normal   N(0, 1)
   normal_k N(0, 1) / sqrt(K)
 Batched operands are drawn as one (batch, rows, cols) tensor.
+
+8-bit operands (``make_f8_inputs``): A (M x K) then B (N x K) drawn as above
+and converted by torch to float8_e4m3fn / float8_e5m2 (round to nearest even);
+then, when asked for, the E8M0 block-scale bytes of A and of B, uniform
+integers in [127 - spread, 127 + spread], and the float32 row scales of A and
+of B, uniform in [0.5, 2).
 """
 from dataclasses import dataclass
 import math
@@ -22,6 +28,7 @@ import numpy as np
 import torch
 
 TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+F8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
 @dataclass(frozen=True)
@@ -116,3 +123,24 @@ def sample_rows(M: int, band: int = 256, extra: int = 64, seed: int = 12345) -> 
     rng = np.random.default_rng(seed)
     rows.update(int(r) for r in rng.integers(0, M, size=extra))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def make_f8_inputs(M: int, N: int, K: int, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                   dist: str = "normal", seed: int = 0, block_scales: bool = False, spread: int = 4,
+                   row_scales: bool = False, block: int = 32):
+    """8-bit TN operands as numpy uint8 bit patterns: A (M, K), B (N, K); block
+    scales xa (M, cdiv(K, block)), xb (N, cdiv(K, block)) or None; row scales
+    sa (M,), sb (N,) float32 or None."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed(seed)
+    a = _draw(gen, (M, K), dist, K).to(F8_TORCH[a_fmt]).view(torch.uint8).numpy().copy()
+    b = _draw(gen, (N, K), dist, K).to(F8_TORCH[b_fmt]).view(torch.uint8).numpy().copy()
+    xa = xb = sa = sb = None
+    nb = (K + block - 1) // block
+    if block_scales:
+        xa = torch.randint(127 - spread, 128 + spread, (M, nb), generator=gen).to(torch.uint8).numpy()
+        xb = torch.randint(127 - spread, 128 + spread, (N, nb), generator=gen).to(torch.uint8).numpy()
+    if row_scales:
+        sa = (torch.rand((M,), generator=gen) * 1.5 + 0.5).numpy()
+        sb = (torch.rand((N,), generator=gen) * 1.5 + 0.5).numpy()
+    return a, b, xa, xb, sa, sb
