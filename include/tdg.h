@@ -54,9 +54,10 @@
 extern "C" {
 #endif
 
-#define TDG_ABI_VERSION 3
+#define TDG_ABI_VERSION 4
 
-typedef enum { TDG_F16 = 0, TDG_BF16 = 1, TDG_F32 = 2 } tdg_dtype;
+/* TDG_E4M3 and TDG_E5M2 are the 8-bit operand types of tdg_gemm_f8 only. */
+typedef enum { TDG_F16 = 0, TDG_BF16 = 1, TDG_F32 = 2, TDG_E4M3 = 3, TDG_E5M2 = 4 } tdg_dtype;
 
 typedef enum {
     TDG_SUCCESS = 0,
@@ -209,6 +210,54 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K,
                       const void *A, int64_t lda, const void *B, int64_t ldb,
                       const void *C, int64_t ldc, int64_t batch,
                       tdg_dtype ab_type, tdg_dtype c_type);
+
+/* 8-bit floating-point operands with scales.  The Croqtile tutorial,
+ * chapter 4 (the variants after the four-step rhythm: quantised operands
+ * with per-tile scaling), has FP8 operands (f8_e4m3, f8_e5m2) whose scales
+ * multiply the contraction after it is formed, in the same kernel -- fused
+ * into the contraction, or as a separate statement on the accumulator.  The
+ * bit layouts are the OCP 8-bit formats: E4M3 (bias 7, no infinities,
+ * S.1111.111 is NaN, largest finite 448) and E5M2 (bias 15, IEEE-like
+ * infinities and NaNs); both with subnormals.
+ *
+ * C (M x N) = A * B^T with A stored M x K and B stored N x K (row-major, row
+ * strides lda, ldb >= K, in bytes = elements), fp32 accumulation:
+ *   C[i,j] = sa(i) * sb(j) * sum_t xa(i,t) * xb(j,t) * sum_{k in block t} A[i,k] * B[j,k]
+ * where block t is k = 32t .. min(32t+32, K) - 1 and
+ *   xa(i,t) = 2^(block_scale_a[i * ld_bsa + t] - 127)   E8M0 bytes, 1 if NULL
+ *   xb(j,t) = 2^(block_scale_b[j * ld_bsb + t] - 127)   (likewise)
+ *   sa(i)   = scale_a[i * inc_a]   fp32; inc_a 0 = one scale for A; 1 if NULL
+ *   sb(j)   = scale_b[j * inc_b]   (likewise for the rows of B)
+ * The block scales are the scale operands of the MFMA itself (the fused
+ * form, 32-element blocks as the gfx950 instruction takes them); the row
+ * scales multiply the fp32 sums in the epilogue (the separate statement),
+ * before the conversion to c_type (round to nearest even).  The E8M0 byte
+ * 0xFF (NaN) is not a valid scale.
+ *
+ * a_type, b_type: TDG_E4M3 or TDG_E5M2, independently.  c_type: TDG_F16,
+ * TDG_BF16 or TDG_F32.  transc 1 stores C transposed: N x M, ldc >= M,
+ * element (i, j) at C[j * ldc + i] (the product with the operands and their
+ * scales exchanged).  config: -1 for the library's choice, or an index in
+ * [0, tdg_f8_num_configs()).
+ * Requirements, else TDG_NOT_SUPPORTED: A and B 16-byte aligned, lda, ldb
+ * and K multiples of 16; block-scale arrays 4-byte aligned with ld_bsa,
+ * ld_bsb multiples of 4 (and >= ceil(K/32), else TDG_INVALID_VALUE), each
+ * an M x ld_bsa (N x ld_bsb) byte array of which only the first ceil(K/32)
+ * bytes of a row are used.  Row scales 4-byte aligned.
+ * Ownership, errors and degenerate sizes as for the other calls (K == 0
+ * writes zeros; M == 0 or N == 0 does nothing). */
+tdg_status tdg_gemm_f8(int transc, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, tdg_dtype a_type,
+                       const void *B, int64_t ldb, tdg_dtype b_type,
+                       const void *block_scale_a, int64_t ld_bsa,
+                       const void *block_scale_b, int64_t ld_bsb,
+                       const float *scale_a, int64_t inc_a,
+                       const float *scale_b, int64_t inc_b,
+                       void *C, int64_t ldc, tdg_dtype c_type, int config, void *stream);
+
+/* Number of 8-bit tile configurations and the name of one (NULL out of range). */
+int tdg_f8_num_configs(void);
+const char *tdg_f8_config_name(int config);
 
 const char *tdg_status_string(tdg_status status);
 /* Human-readable cause of this thread's most recent non-success ("" if none). */

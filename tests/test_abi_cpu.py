@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(tdg):
 
 
 def test_version_configs_and_status_strings(tdg):
-    assert tdg.tdg_abi_version() == 3
+    assert tdg.tdg_abi_version() == 4
     n = tdg.tdg_num_configs()
     assert n >= 2
     names = [tdg.tdg_config_name(i) for i in range(n)]
@@ -180,3 +180,56 @@ def test_general_entry_point_checks(tdg):
     assert g(0, 0, 1, 16, 24, 24) == tdg.TDG_INVALID_VALUE and "ldc" in tdg.tdg_last_error()   # C is N x M: ldc >= 40
     assert g(2, 0, 0, 16, 24, 24) == tdg.TDG_INVALID_VALUE
     assert g(0, 0, 2, 16, 24, 24) == tdg.TDG_INVALID_VALUE
+
+
+def test_f8_configs(tdg):
+    n = tdg.tdg_f8_num_configs()
+    names = [tdg.tdg_f8_config_name(i) for i in range(n)]
+    assert n >= 2 and all(names) and len(set(names)) == n
+    assert tdg.tdg_f8_config_name(n) is None and tdg.tdg_f8_config_name(-1) is None
+
+
+def _f8_call(tdg, **kw):
+    a = dict(transc=0, M=64, N=64, K=128, A=P, lda=128, a_type=tdg.TDG_E4M3, B=P, ldb=128, b_type=tdg.TDG_E4M3,
+             block_scale_a=None, ld_bsa=0, block_scale_b=None, ld_bsb=0, scale_a=None, inc_a=0, scale_b=None,
+             inc_b=0, C=P, ldc=64, c_type=tdg.TDG_F32, config=-1, stream=None)
+    a.update(kw)
+    return tdg.tdg_gemm_f8(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(transc=2), "INVALID", "transc"),
+    (dict(M=-1), "INVALID", "negative"),
+    (dict(K=-16), "INVALID", "negative"),
+    (dict(a_type=0), "INVALID", "a_type"),
+    (dict(b_type=2), "INVALID", "a_type"),
+    (dict(c_type=3), "INVALID", "c_type"),
+    (dict(lda=64), "INVALID", "lda"),
+    (dict(ldb=112), "INVALID", "lda"),
+    (dict(ldc=32), "INVALID", "ldc"),
+    (dict(transc=1, M=128, ldc=64), "INVALID", "ldc"),
+    (dict(block_scale_a=P, ld_bsa=2), "INVALID", "ceil(K/32)"),
+    (dict(block_scale_b=P, ld_bsb=0), "INVALID", "ceil(K/32)"),
+    (dict(inc_a=-1), "INVALID", "increments"),
+    (dict(config=7), "INVALID", "config"),
+    (dict(C=None), "INVALID", "NULL"),
+    (dict(B=None), "INVALID", "NULL"),
+    (dict(C=P + 2, c_type=2), "INVALID", "aligned"),
+    (dict(scale_a=P + 2), "INVALID", "4-byte"),
+    (dict(A=P + 8), "NOT_SUPPORTED", "16-byte"),
+    (dict(lda=136), "NOT_SUPPORTED", "multiples of 16"),
+    (dict(K=120, lda=128, ldb=128), "NOT_SUPPORTED", "multiples of 16"),
+    (dict(block_scale_a=P + 2, ld_bsa=4), "NOT_SUPPORTED", "4-byte"),
+    (dict(block_scale_b=P, ld_bsb=6), "NOT_SUPPORTED", "multiple of 4"),
+    (dict(lda=1 << 24, ldb=1 << 24), "NOT_SUPPORTED", "32-bit"),
+])
+def test_f8_invalid_arguments_rejected_before_launch(tdg, kw, status, needle):
+    st = _f8_call(tdg, **kw)
+    expect = tdg.TDG_INVALID_VALUE if status == "INVALID" else tdg.TDG_NOT_SUPPORTED
+    assert st == expect, (st, tdg.tdg_last_error())
+    assert needle in tdg.tdg_last_error()
+
+
+def test_f8_degenerate_sizes_succeed_without_a_device(tdg):
+    assert _f8_call(tdg, M=0) == tdg.TDG_SUCCESS
+    assert _f8_call(tdg, N=0, A=None, B=None, C=None) == tdg.TDG_SUCCESS

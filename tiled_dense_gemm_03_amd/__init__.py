@@ -10,6 +10,8 @@ and friends); torch supplies device memory and the stream only.
 from ._binding import (  # noqa: F401
     EXPORTED,
     TDG_BF16,
+    TDG_E4M3,
+    TDG_E5M2,
     TDG_F16,
     TDG_F32,
     TDG_INVALID_VALUE,
@@ -20,8 +22,11 @@ from ._binding import (  # noqa: F401
     tdg_autotune,
     tdg_autotune_clear,
     tdg_config_name,
+    tdg_f8_config_name,
+    tdg_f8_num_configs,
     tdg_gemm,
     tdg_gemm_ex,
+    tdg_gemm_f8,
     tdg_gemm_nn,
     tdg_gemm_nn_batched,
     tdg_gemm_tn,
@@ -33,4 +38,4 @@ from ._binding import (  # noqa: F401
     tdg_select_config,
     tdg_status_string,
 )
-from .api import TdgError, autotune, config_names, gemm, select_config  # noqa: F401
+from .api import TdgError, autotune, config_names, gemm, gemm_f8, select_config  # noqa: F401

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtdg.so")
 
-TDG_F16, TDG_BF16, TDG_F32 = 0, 1, 2
+TDG_F16, TDG_BF16, TDG_F32, TDG_E4M3, TDG_E5M2 = 0, 1, 2, 3, 4
 TDG_SUCCESS, TDG_INVALID_VALUE, TDG_NOT_SUPPORTED, TDG_LAUNCH_FAILED = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
@@ -43,6 +43,10 @@ _SIG = {
     "tdg_autotune": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                             _i64, _int, _int, _vp, _sz, _int, ctypes.POINTER(_int), _vp]),
     "tdg_autotune_clear": (None, []),
+    "tdg_gemm_f8": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _vp, _i64, _vp, _i64,
+                           _vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp]),
+    "tdg_f8_num_configs": (_int, []),
+    "tdg_f8_config_name": (ctypes.c_char_p, [_int]),
     "tdg_num_configs": (_int, []),
     "tdg_config_name": (ctypes.c_char_p, [_int]),
     "tdg_select_config": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _int]),
@@ -111,6 +115,21 @@ def tdg_autotune(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strid
 
 def tdg_autotune_clear():
     lib.tdg_autotune_clear()
+
+
+def tdg_gemm_f8(transc, M, N, K, A, lda, a_type, B, ldb, b_type, block_scale_a, ld_bsa, block_scale_b, ld_bsb,
+                scale_a, inc_a, scale_b, inc_b, C, ldc, c_type, config, stream):
+    return lib.tdg_gemm_f8(transc, M, N, K, A, lda, a_type, B, ldb, b_type, block_scale_a, ld_bsa, block_scale_b,
+                           ld_bsb, scale_a, inc_a, scale_b, inc_b, C, ldc, c_type, config, stream)
+
+
+def tdg_f8_num_configs():
+    return lib.tdg_f8_num_configs()
+
+
+def tdg_f8_config_name(config):
+    r = lib.tdg_f8_config_name(config)
+    return None if r is None else r.decode()
 
 
 def tdg_num_configs():

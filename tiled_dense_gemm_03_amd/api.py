@@ -171,3 +171,77 @@ def autotune(a, b, layout="nn", out_dtype=None, out=None, reps=10):
                                ws.data_ptr() if ws is not None else None,
                                ws.numel() if ws is not None else 0, int(reps), best, stream))
     return "auto" if best.value < 0 else _b.tdg_config_name(best.value)
+
+
+_F8 = {torch.float8_e4m3fn: _b.TDG_E4M3, torch.float8_e5m2: _b.TDG_E5M2}
+_F8_NAME = {"e4m3": _b.TDG_E4M3, "e5m2": _b.TDG_E5M2}
+
+
+def _f8_operand(t, fmt, name):
+    """(dtype code, tensor) for an 8-bit operand: a float8 tensor, or a uint8
+    tensor of bit patterns with its format named by `fmt`."""
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be a 2-D row-major tensor" % name)
+    if t.dtype in _F8:
+        return _F8[t.dtype]
+    if t.dtype == torch.uint8 and fmt in _F8_NAME:
+        return _F8_NAME[fmt]
+    raise ValueError("%s must be float8_e4m3fn / float8_e5m2, or uint8 with its format given" % name)
+
+
+def _f8_marshal(a, b, a_fmt, b_fmt, block_scale_a, block_scale_b, scale_a, scale_b, out, out_dtype, transc):
+    at = _f8_operand(a, a_fmt, "a")
+    bt = _f8_operand(b, b_fmt, "b")
+    M, K = a.shape
+    N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ: A has K=%d, B has K=%d" % (K, Kb))
+    shape = (N, M) if transc else (M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype or torch.float32, device=a.device)
+    if out.dtype not in _CT or tuple(out.shape) != shape or (out.size(1) > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a row-major %s tensor of fp16/bf16/fp32" % (shape,))
+
+    def blk(x, rows, name):
+        if x is None:
+            return None, 0
+        if x.dtype != torch.uint8 or x.dim() != 2 or x.size(0) != rows or (x.size(1) > 1 and x.stride(1) != 1):
+            raise ValueError("%s must be a row-major uint8 (rows, ceil(K/32)) tensor of E8M0 bytes" % name)
+        return x.data_ptr(), max(x.stride(0), x.size(1))
+
+    def row(x, rows, name):
+        if x is None:
+            return None, 0
+        if x.dtype != torch.float32 or x.dim() != 1 or x.numel() not in (1, rows):
+            raise ValueError("%s must be a float32 tensor of 1 or %d entries" % (name, rows))
+        return x.data_ptr(), (0 if x.numel() == 1 else x.stride(0))
+
+    xa, ldxa = blk(block_scale_a, M, "block_scale_a")
+    xb, ldxb = blk(block_scale_b, N, "block_scale_b")
+    sa, inca = row(scale_a, M, "scale_a")
+    sb, incb = row(scale_b, N, "scale_b")
+    lda = max(a.stride(0), K, 1)
+    ldb = max(b.stride(0), K, 1)
+    ldc = max(out.stride(0), shape[1], 1)
+    args = (int(bool(transc)), M, N, K, a.data_ptr(), lda, at, b.data_ptr(), ldb, bt, xa, ldxa, xb, ldxb,
+            sa, inca, sb, incb, out.data_ptr(), ldc, _CT[out.dtype])
+    return out, args
+
+
+def gemm_f8(a, b, *, a_fmt=None, b_fmt=None, block_scale_a=None, block_scale_b=None, scale_a=None, scale_b=None,
+            out_dtype=None, out=None, transc=False, config=-1):
+    """8-bit TN product ``C = scale_a[:, None] * scale_b[None, :] * (A B^T)``
+    with optional E8M0 block scales per 32 elements of K (see ``tdg.h``).
+
+    ``a`` (M, K) and ``b`` (N, K): float8_e4m3fn / float8_e5m2 tensors, or
+    uint8 bit patterns with ``a_fmt`` / ``b_fmt`` in {"e4m3", "e5m2"}.
+    ``block_scale_a`` (M, ceil(K/32)) and ``block_scale_b`` (N, ceil(K/32)):
+    uint8 E8M0 bytes (row stride a multiple of 4).  ``scale_a`` (M,) or (1,),
+    ``scale_b`` (N,) or (1,): float32.  ``transc``: return / write C^T
+    (N, M).  Returns ``out`` (a new fp32 tensor unless ``out_dtype`` or
+    ``out`` say otherwise)."""
+    out, args = _f8_marshal(a, b, a_fmt, b_fmt, block_scale_a, block_scale_b, scale_a, scale_b, out, out_dtype,
+                            transc)
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    _check(_b.tdg_gemm_f8(*args, config, stream))
+    return out

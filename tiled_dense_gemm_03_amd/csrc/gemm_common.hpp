@@ -26,6 +26,22 @@ struct GemmArgs {
     int sk_split;
 };
 
+// Kernel arguments of the 8-bit product C = A * B^T (A M x K, B N x K, both
+// K-contiguous; strides in elements = bytes for A and B).
+struct F8Args {
+    const uint8_t *A;
+    const uint8_t *B;
+    void *C;
+    int64_t lda, ldb, ldc;
+    const uint8_t *xa, *xb;      // E8M0 scales, one byte per row and 32-element K block (or null)
+    int64_t ldxa, ldxb;          // bytes between rows of xa / xb (multiples of 4)
+    const float *sa, *sb;        // fp32 scales per row of A / row of B (or null)
+    int64_t inc_sa, inc_sb;      // 0: one scale for every row
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int tiles_per_batch;         // tiles_m * tiles_n (one problem)
+};
+
 }  // namespace tdg
 
 // X(id, KIND, BM, BN, BK, ST, WM, WN, VEC, name): ids run 0, 1, 2, ... in
@@ -50,3 +66,8 @@ struct GemmArgs {
     X(11, 2, 128, 128, 64, 4, 2, 2, true, "128x128x64_s4_w2x2_m16")          \
     X(12, 2, 128, 128, 64, 4, 2, 4, true, "128x128x64_s4_w2x4_m16")          \
     X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")
+
+// 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
+#define TDG_F8_CONFIG_LIST(X)                                   \
+    X(0, 256, 256, 2, 2, 4, "f8_256x256x128_s2_w2x4")          \
+    X(1, 128, 128, 4, 2, 2, "f8_128x128x128_s4_w2x2")

@@ -105,7 +105,8 @@ __device__ __forceinline__ int xcd_order(int w, int num) {
 // Logical tile index -> (problem, tile row, tile column).  Tiles are ordered
 // in groups of GROUP_M tile rows, column by column inside a group, so a burst
 // of concurrent tiles covers a compact block of the output.
-__device__ __forceinline__ void tile_of(const GemmArgs &p, int logical, int &batch, int &tm, int &tn) {
+template <class Args>
+__device__ __forceinline__ void tile_of(const Args &p, int logical, int &batch, int &tm, int &tn) {
     batch = logical / p.tiles_per_batch;
     const int t = logical - batch * p.tiles_per_batch;
     const int group_size = GROUP_M * p.tiles_n;

@@ -26,6 +26,10 @@ hipError_t launch_t0_ab0(int cfg, int ct, int transa, const GemmArgs &a, int64_t
 hipError_t launch_t0_ab1(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_t1_ab0(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_t1_ab1(int cfg, int ct, int transa, const GemmArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_f8_a0_b0(int cfg, int ct, int bscale, const F8Args &a, int64_t grid, hipStream_t s);
+hipError_t launch_f8_a0_b1(int cfg, int ct, int bscale, const F8Args &a, int64_t grid, hipStream_t s);
+hipError_t launch_f8_a1_b0(int cfg, int ct, int bscale, const F8Args &a, int64_t grid, hipStream_t s);
+hipError_t launch_f8_a1_b1(int cfg, int ct, int bscale, const F8Args &a, int64_t grid, hipStream_t s);
 
 namespace {
 
@@ -447,10 +451,135 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
                   stream, tuned ? nullptr : ws, tuned ? 0 : ws_bytes, cus);
 }
 
+// ---- 8-bit operands ----
+
+struct F8Config {
+    int bm, bn, stages, wm, wn;
+    const char *name;
+};
+
+const F8Config kF8Configs[] = {
+#define TDG_F8_ROW(ID, BM, BN, ST, WM, WN, NAME) {BM, BN, ST, WM, WN, NAME},
+    TDG_F8_CONFIG_LIST(TDG_F8_ROW)
+#undef TDG_F8_ROW
+};
+constexpr int kNumF8Configs = (int)(sizeof(kF8Configs) / sizeof(kF8Configs[0]));
+
+constexpr int kF8ConfigIds[] = {
+#define TDG_F8_ID(ID, BM, BN, ST, WM, WN, NAME) ID,
+    TDG_F8_CONFIG_LIST(TDG_F8_ID)
+#undef TDG_F8_ID
+};
+constexpr bool f8_ids_in_order(int i) {
+    return i == kNumF8Configs || (kF8ConfigIds[i] == i && f8_ids_in_order(i + 1));
+}
+static_assert(f8_ids_in_order(0), "8-bit configuration ids must be 0, 1, ... in list order");
+
+bool is_f8(int t) { return t == TDG_E4M3 || t == TDG_E5M2; }
+
+// C = sa * sb * blockscaled(A * B^T), written as C or C^T (see tdg.h).
+// Every argument check comes before the device check, so that argument
+// errors read the same on any host.
+tdg_status run_f8(int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_type, const void *B,
+                  int64_t ldb, int b_type, const void *xa, int64_t ldxa, const void *xb, int64_t ldxb,
+                  const float *sa, int64_t inc_sa, const float *sb, int64_t inc_sb, void *C, int64_t ldc,
+                  int c_type, int config, void *stream) {
+    g_err[0] = '\0';
+    if (transc != 0 && transc != 1) return fail(TDG_INVALID_VALUE, "transc must be 0 or 1");
+    if (M < 0 || N < 0 || K < 0)
+        return fail(TDG_INVALID_VALUE, "negative size (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+                    (long long)K);
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return fail(TDG_INVALID_VALUE, "M, N and K must each be below 2^31");
+    if (!is_f8(a_type) || !is_f8(b_type)) return fail(TDG_INVALID_VALUE, "a_type and b_type must be TDG_E4M3 or TDG_E5M2");
+    if (c_type != TDG_F16 && c_type != TDG_BF16 && c_type != TDG_F32)
+        return fail(TDG_INVALID_VALUE, "c_type must be TDG_F16, TDG_BF16 or TDG_F32");
+    const int64_t kmin = K > 0 ? K : 1, cmin = (transc ? M : N) > 0 ? (transc ? M : N) : 1;
+    const int64_t nkb = (K + 31) / 32, bmin = nkb > 0 ? nkb : 1;
+    if (lda < kmin || ldb < kmin) return fail(TDG_INVALID_VALUE, "lda and ldb must be at least K (%lld)", (long long)K);
+    if (ldc < cmin)
+        return fail(TDG_INVALID_VALUE, "ldc (%lld) < %s (%lld)", (long long)ldc, transc ? "M" : "N", (long long)cmin);
+    if ((xa && ldxa < bmin) || (xb && ldxb < bmin))
+        return fail(TDG_INVALID_VALUE, "block-scale row strides must be at least ceil(K/32) = %lld", (long long)nkb);
+    if (inc_sa < 0 || inc_sb < 0) return fail(TDG_INVALID_VALUE, "row-scale increments must be nonnegative");
+    if (config < -1 || config >= kNumF8Configs)
+        return fail(TDG_INVALID_VALUE, "config %d out of range [-1, %d)", config, kNumF8Configs);
+    if (M == 0 || N == 0) return TDG_SUCCESS;
+    if (C == nullptr) return fail(TDG_INVALID_VALUE, "C is NULL");
+    if (K > 0 && (A == nullptr || B == nullptr)) return fail(TDG_INVALID_VALUE, "A or B is NULL");
+    if ((uintptr_t)C & (c_type == TDG_F32 ? 3u : 1u)) return fail(TDG_INVALID_VALUE, "C must be aligned to its element size");
+    if (((uintptr_t)sa | (uintptr_t)sb) & 3u) return fail(TDG_INVALID_VALUE, "row scales must be 4-byte aligned");
+    if (K > 0 && (!aligned16(A) || !aligned16(B) || (lda & 15) || (ldb & 15) || (K & 15)))
+        return fail(TDG_NOT_SUPPORTED,
+                    "8-bit operands need 16-byte aligned A and B, lda, ldb and K multiples of 16");
+    if ((xa && (((uintptr_t)xa & 3u) || (ldxa & 3))) || (xb && (((uintptr_t)xb & 3u) || (ldxb & 3))))
+        return fail(TDG_NOT_SUPPORTED, "block-scale arrays need 4-byte aligned bases and row strides multiple of 4");
+    // 32-bit buffer offsets inside one tile (at most 256 rows of each array)
+    const int64_t lim = (int64_t)1 << 31, es = (c_type == TDG_F32) ? 4 : 2;
+    if (256 * lda >= lim || 256 * ldb >= lim || 256 * ldc * es >= lim || 256 * ldxa >= lim || 256 * ldxb >= lim)
+        return fail(TDG_NOT_SUPPORTED, "a leading dimension is too large for 32-bit in-tile offsets");
+    if (cdiv(M, 128) * cdiv(N, 128) > (int64_t)INT_MAX) return fail(TDG_INVALID_VALUE, "too many output tiles");
+    int cus = 0;
+    tdg_status st = check_device(&cus);
+    if (st != TDG_SUCCESS) return st;
+    if (transc) {   // C^T = B * A^T: exchange the operands with their scales
+        std::swap(M, N);
+        std::swap(A, B);
+        std::swap(lda, ldb);
+        std::swap(a_type, b_type);
+        std::swap(xa, xb);
+        std::swap(ldxa, ldxb);
+        std::swap(sa, sb);
+        std::swap(inc_sa, inc_sb);
+    }
+    if (config < 0) config = (cdiv(M, 256) * cdiv(N, 256) >= cus) ? 0 : 1;
+    const F8Config &cf = kF8Configs[config];
+    F8Args a;
+    a.A = static_cast<const uint8_t *>(A);
+    a.B = static_cast<const uint8_t *>(B);
+    a.C = C;
+    a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+    a.xa = static_cast<const uint8_t *>(xa);
+    a.xb = static_cast<const uint8_t *>(xb);
+    a.ldxa = ldxa; a.ldxb = ldxb;
+    a.sa = sa; a.sb = sb;
+    a.inc_sa = inc_sa; a.inc_sb = inc_sb;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.tiles_m = (int)cdiv(M, cf.bm);
+    a.tiles_n = (int)cdiv(N, cf.bn);
+    a.tiles_per_batch = a.tiles_m * a.tiles_n;
+    const int64_t grid = a.tiles_per_batch;
+    const int bscale = (xa != nullptr || xb != nullptr) ? 1 : 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int fa = a_type == TDG_E5M2, fb = b_type == TDG_E5M2;
+    hipError_t e;
+    if (fa == 0)
+        e = fb == 0 ? launch_f8_a0_b0(config, c_type, bscale, a, grid, s) : launch_f8_a0_b1(config, c_type, bscale, a, grid, s);
+    else
+        e = fb == 0 ? launch_f8_a1_b0(config, c_type, bscale, a, grid, s) : launch_f8_a1_b1(config, c_type, bscale, a, grid, s);
+    if (e != hipSuccess) return fail(TDG_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+    return TDG_SUCCESS;
+}
+
 }  // namespace
 }  // namespace tdg
 
 extern "C" {
+
+tdg_status tdg_gemm_f8(int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, tdg_dtype a_type,
+                       const void *B, int64_t ldb, tdg_dtype b_type, const void *block_scale_a, int64_t ld_bsa,
+                       const void *block_scale_b, int64_t ld_bsb, const float *scale_a, int64_t inc_a,
+                       const float *scale_b, int64_t inc_b, void *C, int64_t ldc, tdg_dtype c_type, int config,
+                       void *stream) {
+    return tdg::run_f8(transc, M, N, K, A, lda, a_type, B, ldb, b_type, block_scale_a, ld_bsa, block_scale_b, ld_bsb,
+                       scale_a, inc_a, scale_b, inc_b, C, ldc, c_type, config, stream);
+}
+
+int tdg_f8_num_configs(void) { return tdg::kNumF8Configs; }
+
+const char *tdg_f8_config_name(int config) {
+    if (config < 0 || config >= tdg::kNumF8Configs) return nullptr;
+    return tdg::kF8Configs[config].name;
+}
 
 tdg_status tdg_gemm_nn(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
                        void *C, int64_t ldc, tdg_dtype ab_type, tdg_dtype c_type, void *stream) {
