@@ -240,8 +240,8 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K,
  * scales exchanged).  config: -1 for the library's choice, or an index in
  * [0, tdg_f8_num_configs()).
  * Requirements, else TDG_NOT_SUPPORTED: A and B 16-byte aligned, lda, ldb
- * and K multiples of 16; block-scale arrays 4-byte aligned with ld_bsa,
- * ld_bsb multiples of 4 (and >= ceil(K/32), else TDG_INVALID_VALUE), each
+ * and K multiples of 16; block-scale arrays 16-byte aligned with ld_bsa,
+ * ld_bsb multiples of 16 (and >= ceil(K/32), else TDG_INVALID_VALUE), each
  * an M x ld_bsa (N x ld_bsb) byte array of which only the first ceil(K/32)
  * bytes of a row are used.  Row scales 4-byte aligned.
  * Ownership, errors and degenerate sizes as for the other calls (K == 0

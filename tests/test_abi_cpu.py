@@ -219,8 +219,8 @@ def _f8_call(tdg, **kw):
     (dict(A=P + 8), "NOT_SUPPORTED", "16-byte"),
     (dict(lda=136), "NOT_SUPPORTED", "multiples of 16"),
     (dict(K=120, lda=128, ldb=128), "NOT_SUPPORTED", "multiples of 16"),
-    (dict(block_scale_a=P + 2, ld_bsa=4), "NOT_SUPPORTED", "4-byte"),
-    (dict(block_scale_b=P, ld_bsb=6), "NOT_SUPPORTED", "multiple of 4"),
+    (dict(block_scale_a=P + 4, ld_bsa=16), "NOT_SUPPORTED", "16-byte"),
+    (dict(block_scale_b=P, ld_bsb=8), "NOT_SUPPORTED", "multiple of 16"),
     (dict(lda=1 << 24, ldb=1 << 24), "NOT_SUPPORTED", "32-bit"),
 ])
 def test_f8_invalid_arguments_rejected_before_launch(tdg, kw, status, needle):

@@ -51,14 +51,14 @@ def pad_cols(x, mult):
 
 def gpu_f8(tdg, a, b, afmt, bfmt, xa=None, xb=None, sa=None, sb=None, out="f32", transc=False, config=-1):
     """Run the library on host arrays (block-scale rows padded to a stride
-    that is a multiple of 4 with NaN bytes) and return the CPU result."""
+    that is a multiple of 16 with NaN bytes) and return the CPU result."""
     ad, bd = dev(a), dev(b)
     xad = xbd = None
     if xa is not None:
-        xp, cols = pad_cols(xa, 4)
+        xp, cols = pad_cols(xa, 16)
         xad = dev(xp)[:, :cols]
     if xb is not None:
-        xp, cols = pad_cols(xb, 4)
+        xp, cols = pad_cols(xb, 16)
         xbd = dev(xp)[:, :cols]
     c = tdg.gemm_f8(ad, bd, a_fmt=afmt, b_fmt=bfmt, block_scale_a=xad, block_scale_b=xbd,
                     scale_a=dev(sa), scale_b=dev(sb), out_dtype=OUT_TORCH[out], transc=transc, config=config)
@@ -164,12 +164,12 @@ def test_f8_output_ownership_and_strides(tdg):
     ap, _ = pad_cols(a, 64)
     bp, _ = pad_cols(b, 48)
     ad, bd = dev(ap)[:, :K], dev(bp)[:, :K]
-    xap, _ = pad_cols(xa, 8)
+    xap, _ = pad_cols(xa, 32)
     xad = dev(xap)[:, :xa.shape[1]]
     ldc = N + 24
     buf = torch.full((M + 3, ldc), float("nan"), device="cuda")
     out = buf[1:M + 1, :N]
-    tdg.gemm_f8(ad, bd, a_fmt="e4m3", b_fmt="e4m3", block_scale_a=xad, block_scale_b=dev(pad_cols(xb, 4)[0]),
+    tdg.gemm_f8(ad, bd, a_fmt="e4m3", b_fmt="e4m3", block_scale_a=xad, block_scale_b=dev(pad_cols(xb, 16)[0]),
                 out=out)
     torch.cuda.synchronize()
     host = buf.cpu()

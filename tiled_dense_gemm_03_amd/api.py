@@ -236,7 +236,7 @@ def gemm_f8(a, b, *, a_fmt=None, b_fmt=None, block_scale_a=None, block_scale_b=N
     ``a`` (M, K) and ``b`` (N, K): float8_e4m3fn / float8_e5m2 tensors, or
     uint8 bit patterns with ``a_fmt`` / ``b_fmt`` in {"e4m3", "e5m2"}.
     ``block_scale_a`` (M, ceil(K/32)) and ``block_scale_b`` (N, ceil(K/32)):
-    uint8 E8M0 bytes (row stride a multiple of 4).  ``scale_a`` (M,) or (1,),
+    uint8 E8M0 bytes (16-byte aligned, row stride a multiple of 16).  ``scale_a`` (M,) or (1,),
     ``scale_b`` (N,) or (1,): float32.  ``transc``: return / write C^T
     (N, M).  Returns ``out`` (a new fp32 tensor unless ``out_dtype`` or
     ``out`` say otherwise)."""

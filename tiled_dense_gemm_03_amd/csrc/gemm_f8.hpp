@@ -35,9 +35,14 @@
 // K step ks (0, 1) of a K tile covers k = 64 ks .. 64 ks + 63: lane l reads
 // granules 4 ks + g and 4 ks + 2 + g of its row, and its scale must be the
 // one of block 4 kt + 2 ks + g of the whole K range.  The four block-scale
-// bytes of a row for K tile kt are one aligned dword of the scale array; it
-// travels with the tile (a 4-byte direct load per row into the stage), each
-// lane shifts its copy right by 8 g bits, and op_sel = 2 ks picks the byte.
+// bytes of a row for K tile kt are dword kt % 4 of the row's 16 bytes for
+// K tiles 4h .. 4h + 3 (h = kt / 4); those 16 bytes of every row of the
+// workgroup's A and B tiles travel to LDS together (one direct 16-byte load
+// per row, with the data of K tile 4h) into one of two group buffers.  At
+// the start of K tile kt each lane reads its dwords for the tile and packs
+// two fragments' bytes into one register with one byte permute: bytes
+// (g, 2 + g) of fragment 2p at positions (0, 2), those of fragment 2p + 1
+// at (1, 3); op_sel = 2 ks + (fragment % 2) then picks the scale.
 #pragma once
 
 #include "gemm_m16.hpp"
@@ -48,28 +53,31 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // One scaled 32 x 32 x 64 MFMA: first operand x of format FX with scale byte
-// OP of sx, second operand y of format FY with scale byte OP of sy (formats:
-// 0 = E4M3, 1 = E5M2).
-template <int FX, int FY, int OP>
+// OPX of sx, second operand y of format FY with scale byte OPY of sy
+// (formats: 0 = E4M3, 1 = E5M2).
+template <int FX, int FY, int OPX, int OPY>
 __device__ __forceinline__ f32x16 mfma_f8(u32x4 xl, u32x4 xh, u32x4 yl, u32x4 yh, f32x16 c, int sx, int sy) {
     const i32x8 x = __builtin_bit_cast(i32x8, __builtin_shufflevector(xl, xh, 0, 1, 2, 3, 4, 5, 6, 7));
     const i32x8 y = __builtin_bit_cast(i32x8, __builtin_shufflevector(yl, yh, 0, 1, 2, 3, 4, 5, 6, 7));
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, OP, sx, OP, sy);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, OPX, sx, OPY, sy);
 }
 
-// One direct global -> LDS load of 4 bytes per lane: lane l's dword at byte
-// offset voff lands at LDS address lds_base + IMM + 4*l (zero for an
-// out-of-range offset).  Same conventions as dma16.
+// dma16 issued only when `issue` (wave-uniform) is nonzero.  The test and
+// the skip are inside the assembly, so the kernel's code around it stays one
+// basic block and the compiler's instruction schedule is not split there.
 template <uint32_t IMM>
-__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+__device__ __forceinline__ void dma16_if(u32x4 rsrc, uint32_t voff, uint32_t lds_base, uint32_t issue) {
     uint32_t saved;
     asm volatile(
+        "s_cmp_eq_u32 %5, 0\n\t"
+        "s_cbranch_scc1 1f\n\t"
         "s_mov_b32 %0, m0\n\t"
         "s_add_u32 m0, %3, %4\n\t"
-        "buffer_load_dword %1, %2, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0\n"
+        "1:"
         : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(lds_base), "n"(IMM)
+        : "v"(voff), "s"(rsrc), "s"(lds_base), "n"(IMM), "s"(issue)
         : "memory", "scc");
 }
 
@@ -88,19 +96,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int RM = WTM / 32, RN = WTN / 32;
     static_assert(RM * 32 == WTM && RN * 32 == WTN, "wave tile must be a multiple of 32");
+    static_assert(RM % 2 == 0 && RN % 2 == 0, "fragments pair up for the packed scales");
     static_assert(NW % 2 == 0, "an even number of waves");
     constexpr int A_SLOTS = BM * KG, B_SLOTS = BN * KG;
-    constexpr int S_SLOTS = BSCALE ? (BM + BN) / 4 : 0;   // one scale dword per row of the tile
-    constexpr int STAGE = A_SLOTS + B_SLOTS + S_SLOTS;
+    constexpr int STAGE = A_SLOTS + B_SLOTS;
+    constexpr int SG = BSCALE ? BM + BN : 0;        // slots of one scale group buffer (16 bytes per row)
     constexpr int NIA = A_SLOTS / 64, NIB = B_SLOTS / 64, NIS = BSCALE ? (BM + BN) / 64 : 0;
     static_assert(NIA % NW == 0 && NIB % NW == 0 && NIS % NW == 0, "whole load instructions per wave");
-    constexpr int QA = NIA / NW, QB = NIB / NW, QS = NIS / NW, NDMA = QA + QB + QS;
+    constexpr int QA = NIA / NW, QB = NIB / NW, QS = NIS / NW, NDMA = QA + QB;
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
-    static_assert((STAGES - 1) * NDMA < 64, "vmcnt range");
-    static_assert(STAGE * 16 * STAGES <= 160 * 1024, "LDS budget");
-    constexpr uint32_t SOFF = (uint32_t)(A_SLOTS + B_SLOTS) * 16u;   // byte offset of a stage's scales
+    static_assert((STAGES - 1) * NDMA + 1 < 64, "vmcnt range");
+    static_assert((STAGE * STAGES + 2 * SG) * 16 <= 160 * 1024, "LDS budget");
+    constexpr uint32_t SOFF = (uint32_t)(STAGE * STAGES) * 16u;   // byte offset of the scale group buffers
 
-    __shared__ u32x4 smem[STAGES * STAGE];
+    __shared__ u32x4 smem[STAGES * STAGE + 2 * SG];
 
     int batch, tm, tn;
     tile_of(p, xcd_order(blockIdx.x, gridDim.x), batch, tm, tn);
@@ -132,8 +141,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
     const uint32_t b_lane = (uint32_t)(kc_row * ldb + kc_g * 16);
     const uint32_t b_qs = (uint32_t)(NW * 8 * ldb);
     // Scale load q of this wave is instruction t = q*NW + wave over the rows
-    // of A (t < BM/64) then of B: lane l fetches the K tile's scale dword of
-    // row 64 t' + l, which lands at SOFF + 4 * (row index in the tile list).
+    // of A (t < BM/64) then of B: lane l fetches the 16 scale bytes of K
+    // tiles 4h .. 4h + 3 of row 64 t' + l, which land in group buffer h % 2
+    // at 16 * (row index in the tile list).
     const uint8_t *s_base[QS > 0 ? QS : 1];
     uint32_t s_off[QS > 0 ? QS : 1];
 #pragma unroll
@@ -166,15 +176,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
             const u32x4 rs = rsrc_words_n(Btile + k0, records_bytes((int64_t)(b_rows - 1) * ldb + K - k0));
             const uint32_t off = (k0 < kc_klim ? b_lane : OOB_OFFSET) + (uint32_t)qb * b_qs;
             dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
-        } else {
-            constexpr int qs = q - QA - QB;
-            const uint32_t base = lds_addr_of(st) + (uint32_t)wave * 256u;
-            const u32x4 rs = rsrc_words(s_base[qs] + 4 * kt);
-            const uint32_t off = kt < nk ? s_off[qs] : OOB_OFFSET;
-            dma4<SOFF + (uint32_t)(qs * NW) * 256u>(rs, off, base);
         }
     };
-    auto issue_to = [&](int kt, u32x4 *st) { static_for<0, NDMA>([&](auto q) { dma_op(q, kt, st); }); };
+    // With the data of K tile kt, when kt starts a group of four (and is a
+    // tile of the product), the scale group of K tiles kt .. kt + 3, issued
+    // first so that the waits for tile kt cover it too.
+    auto scale_group = [&](int kt) {
+        if constexpr (BSCALE) {
+            const int h = kt >> 2;
+            const uint32_t issue = __builtin_amdgcn_readfirstlane((uint32_t)(((kt & 3) == 0) & (kt < nk)));
+            const uint32_t base = lds_addr_of(smem) + SOFF + (uint32_t)(h & 1) * (SG * 16u) + (uint32_t)wave * 1024u;
+            static_for<0, QS>([&](auto qtag) {
+                constexpr int qs = decltype(qtag)::value;
+                const u32x4 rs = rsrc_words(s_base[qs] + 16 * h);
+                dma16_if<(uint32_t)(qs * NW) * 1024u>(rs, s_off[qs], base, issue);
+            });
+        }
+    };
+    auto issue_to = [&](int kt, u32x4 *st) {
+        scale_group(kt);
+        static_for<0, NDMA>([&](auto q) { dma_op(q, kt, st); });
+    };
 
     // ---- fragment addresses ----
     // A fragment i, half h at K step ks: row wave_m*WTM + 32 i + lane%32,
@@ -189,24 +211,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
             a_b[ks][h] = (wave_m * WTM + fr) * KG + ((4 * ks + 2 * h + fg) ^ ((fr >> 1) & 7));
             b_b[ks][h] = (wave_n * WTN + fr) * KG + ((4 * ks + 2 * h + fg) ^ ((fr >> 1) & 7));
         }
-    const int sa_w = (int)(SOFF / 4) + wave_m * WTM + fr;          // scale dword of A fragment 0's row
-    const int sb_w = (int)(SOFF / 4) + BM + wave_n * WTN + fr;     // ... of B fragment 0's row
+    const int sa_w = 4 * (wave_m * WTM + fr);              // scale dwords of A fragment 0's row
+    const int sb_w = 4 * (BM + wave_n * WTN + fr);         // ... of B fragment 0's row
+    // the scale dwords of K tile kt: group buffer (kt / 4) % 2, dword kt % 4
+    auto scale_ptr = [&](int kt) {
+        return reinterpret_cast<const uint32_t *>(smem + STAGE * STAGES + ((kt >> 2) & 1) * SG) + (kt & 3);
+    };
 
     constexpr int NFR = 2 * (RM + RN);             // fragment reads per K step
-    constexpr int NSR = BSCALE ? RM + RN : 0;      // scale reads per K tile (with step 0)
     auto frag_op = [&](auto dtag, const u32x4 *st, int ks, u32x4 (&al)[RM], u32x4 (&ah)[RM], u32x4 (&bl)[RN],
-                       u32x4 (&bh)[RN], uint32_t (&sr)[RM + RN]) {
+                       u32x4 (&bh)[RN]) {
         constexpr int d = decltype(dtag)::value;
         if constexpr (d < 2 * RM) {
             constexpr int i = d / 2, h = d % 2;
             (h ? ah : al)[i] = st[a_b[ks][h] + i * 32 * KG];
-        } else if constexpr (d < NFR) {
+        } else {
             constexpr int j = (d - 2 * RM) / 2, h = (d - 2 * RM) % 2;
             (h ? bh : bl)[j] = st[A_SLOTS + b_b[ks][h] + j * 32 * KG];
-        } else {
-            constexpr int e = d - NFR;
-            const uint32_t *sw = reinterpret_cast<const uint32_t *>(st);
-            sr[e] = e < RM ? sw[sa_w + 32 * e] : sw[sb_w + 32 * (e - RM)];
         }
     };
 
@@ -219,27 +240,36 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     u32x4 al[2][RM], ah[2][RM], bl[2][RN], bh[2][RN];
-    uint32_t sraw[RM + RN];
-    int sc[RM + RN];
+    constexpr int NPR = (RM + RN) / 2;             // packed scale registers
+    int sc[NPR];
 #pragma unroll
-    for (int e = 0; e < RM + RN; ++e) { sraw[e] = 0x7f7f7f7fu; sc[e] = 0x7f7f7f7f; }   // every byte: scale 1
+    for (int e = 0; e < NPR; ++e) sc[e] = 0x7f7f7f7f;   // every byte: scale 1
 
-    // The block-scale operands of K tile kt: blocks past the end of K (in
-    // the last tile) get scale 1 -- their operands are zero, and the bytes
-    // there are not part of the caller's scale rows -- then each lane
-    // shifts its dword so that byte 2 ks is its block of step ks.
+    // The block-scale operands of K tile kt, read at the start of its
+    // iteration.  Blocks past the end of K (in the last tile) get scale 1
+    // -- their operands are zero, and those bytes are not part of the
+    // caller's scale rows -- as does an operand without block scales.
+    const bool has_xa = p.xa != nullptr, has_xb = p.xb != nullptr;
+    const uint32_t perm_sel = 0x06020400u + 0x01010101u * (uint32_t)fg;
     auto scales_for = [&](int kt) {
         if constexpr (BSCALE) {
+            const uint32_t *sg = scale_ptr(kt);
+            uint32_t raw[RM + RN];
+#pragma unroll
+            for (int e = 0; e < RM + RN; ++e) raw[e] = e < RM ? sg[sa_w + 128 * e] : sg[sb_w + 128 * (e - RM)];
+            // (uniform masks of the bytes to keep: one bit-field insert each)
             const int rem = nkb - 4 * kt;
-            uint32_t keep = 0xffffffffu;
-            if (rem < 4) keep = rem <= 0 ? 0u : ((1u << (8 * rem)) - 1u);
-            const uint32_t keep_a = p.xa != nullptr ? keep : 0u;
-            const uint32_t keep_b = p.xb != nullptr ? keep : 0u;
+            const uint32_t keep = rem >= 4 ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << (8 * rem)) - 1u));
+            const uint32_t keep_a = has_xa ? keep : 0u;
+            const uint32_t keep_b = has_xb ? keep : 0u;
 #pragma unroll
             for (int e = 0; e < RM + RN; ++e) {
                 const uint32_t k = e < RM ? keep_a : keep_b;
-                sc[e] = (int)(((sraw[e] & k) | (0x7f7f7f7fu & ~k)) >> (8 * fg));
+                raw[e] = (raw[e] & k) | (0x7f7f7f7fu & ~k);
             }
+            // bytes (g, 2+g) of fragment 2p -> (0, 2), of fragment 2p+1 -> (1, 3)
+#pragma unroll
+            for (int e = 0; e < NPR; ++e) sc[e] = (int)__builtin_amdgcn_perm(raw[2 * e + 1], raw[2 * e], perm_sel);
         }
     };
 
@@ -248,7 +278,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
         wait_vm_lgkm0<(STAGES - 1) * NDMA>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        static_for<0, NFR + NSR>([&](auto d) { frag_op(d, smem, 0, al[0], ah[0], bl[0], bh[0], sraw); });
+        static_for<0, NFR>([&](auto d) { frag_op(d, smem, 0, al[0], ah[0], bl[0], bh[0]); });
     }
 
     // One K tile per iteration, as in the 16-bit kernel: step 0's MFMAs with
@@ -262,27 +292,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
         u32x4 *cur = smem + s_cur * STAGE;
         u32x4 *nxt = smem + s_nxt * STAGE;
         scales_for(kt);
-        static_for<0, NFR>([&](auto d) { frag_op(d, cur, 1, al[1], ah[1], bl[1], bh[1], sraw); });
-#pragma unroll
-        for (int i = 0; i < RM; ++i)
-#pragma unroll
-            for (int j = 0; j < RN; ++j)
-                acc[i][j] = mfma_f8<FB, FA, 0>(bl[0][j], bh[0][j], al[0][i], ah[0][i], acc[i][j], sc[RM + j], sc[i]);
+        static_for<0, NFR>([&](auto d) { frag_op(d, cur, 1, al[1], ah[1], bl[1], bh[1]); });
+        static_for<0, NMF>([&](auto m) {
+            constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+            acc[i][j] = mfma_f8<FB, FA, j % 2, i % 2>(bl[0][j], bh[0][j], al[0][i], ah[0][i], acc[i][j],
+                                                      sc[RM / 2 + j / 2], sc[i / 2]);
+        });
         interleave_hint<NMF, NFR>();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         wait_vm_lgkm0<(STAGES - 2) * NDMA>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         constexpr int NSUB = NDMA;
-        constexpr int NDS = NFR + NSR;
         static_for<0, NSUB>([&](auto sub) {
             constexpr int s0 = decltype(sub)::value;
             static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
                 constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
-                acc[i][j] = mfma_f8<FB, FA, 2>(bl[1][j], bh[1][j], al[1][i], ah[1][i], acc[i][j], sc[RM + j], sc[i]);
+                acc[i][j] = mfma_f8<FB, FA, 2 + j % 2, 2 + i % 2>(bl[1][j], bh[1][j], al[1][i], ah[1][i], acc[i][j],
+                                                                  sc[RM / 2 + j / 2], sc[i / 2]);
             });
-            static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>(
-                [&](auto d) { frag_op(d, nxt, 0, al[0], ah[0], bl[0], bh[0], sraw); });
+            static_for<s0 * NFR / NSUB, (s0 + 1) * NFR / NSUB>(
+                [&](auto d) { frag_op(d, nxt, 0, al[0], ah[0], bl[0], bh[0]); });
+            if constexpr (s0 == 0) scale_group(kt + STAGES);
             dma_op(sub, kt + STAGES, cur);
             __builtin_amdgcn_sched_barrier(0);
         });

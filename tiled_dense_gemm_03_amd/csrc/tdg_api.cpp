@@ -511,8 +511,8 @@ tdg_status run_f8(int transc, int64_t M, int64_t N, int64_t K, const void *A, in
     if (K > 0 && (!aligned16(A) || !aligned16(B) || (lda & 15) || (ldb & 15) || (K & 15)))
         return fail(TDG_NOT_SUPPORTED,
                     "8-bit operands need 16-byte aligned A and B, lda, ldb and K multiples of 16");
-    if ((xa && (((uintptr_t)xa & 3u) || (ldxa & 3))) || (xb && (((uintptr_t)xb & 3u) || (ldxb & 3))))
-        return fail(TDG_NOT_SUPPORTED, "block-scale arrays need 4-byte aligned bases and row strides multiple of 4");
+    if ((xa && (!aligned16(xa) || (ldxa & 15))) || (xb && (!aligned16(xb) || (ldxb & 15))))
+        return fail(TDG_NOT_SUPPORTED, "block-scale arrays need 16-byte aligned bases and row strides multiple of 16");
     // 32-bit buffer offsets inside one tile (at most 256 rows of each array)
     const int64_t lim = (int64_t)1 << 31, es = (c_type == TDG_F32) ? 4 : 2;
     if (256 * lda >= lim || 256 * ldb >= lim || 256 * ldc * es >= lim || 256 * ldxa >= lim || 256 * ldxb >= lim)
