@@ -4,8 +4,9 @@
 One step = one call of the library (argument checks, tile-config choice,
 one kernel launch) over the resident inputs of the workload.  Default
 workload: the 8192^3 bf16 NN product with bf16 output (A, B ~ N(0, 1),
-seed 4).  The 4096^3 fp16 NN product is measured alongside (its figure is
-reported under "also").  Inputs are generated on the host, copied to HBM
+seed 4).  The 4096^3 fp16 NN product, the ragged and batched products and
+the 8192^3 E4M3 TN products (with and without block scales) are measured
+alongside (their figures are reported under "also").  Inputs are generated on the host, copied to HBM
 before timing, and stay there.
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps; then K timed steps
@@ -24,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s at 4096³ and 8192³ fp16 (fraction of MFMA peak), 1 MI355X"
-PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16 MFMA, published
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0}   # MI355X dense MFMA, published
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -77,6 +78,47 @@ def time_workload(tdg, torch, w, steps, warmup):
     kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
     cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
     return wall * 1e3 / steps, kernel_ms, tdg.tdg_config_name(cfg)
+
+
+def time_f8_workload(tdg, torch, w, steps, warmup):
+    """As time_workload, for an 8-bit workload (block-scale rows padded to a
+    16-byte multiple, as the library asks)."""
+    import numpy as np
+    from workloads import TORCH_DTYPE, f8_workload_inputs
+    a, b, xa, xb, sa, sb = f8_workload_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def padded(x):
+        if x is None:
+            return None
+        ld = -(-x.shape[1] // 16) * 16
+        p = np.zeros((x.shape[0], ld), dtype=np.uint8)
+        p[:, :x.shape[1]] = x
+        return torch.from_numpy(p).to(dev)[:, :x.shape[1]]
+
+    ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    xad, xbd = padded(xa), padded(xb)
+    sad = None if sa is None else torch.from_numpy(sa).to(dev)
+    sbd = None if sb is None else torch.from_numpy(sb).to(dev)
+    c = torch.empty((w.M, w.N), dtype=TORCH_DTYPE[w.out_dtype], device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        tdg.gemm_f8(ad, bd, a_fmt=w.a_fmt, b_fmt=w.b_fmt, block_scale_a=xad, block_scale_b=xbd, scale_a=sad,
+                    scale_b=sbd, out=c)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    return wall * 1e3 / steps, kernel_ms
 
 
 def cpu_baseline(w, seconds_min=10.0):
@@ -233,6 +275,17 @@ def main():
                 entry["hbm_gbps"] = round(nbytes / (kms_a * 1e-3) / 1e9, 1)
                 entry["hbm_frac"] = round(nbytes / (kms_a * 1e-3) / 1e9 / HBM_GBPS, 4)
             also.append(entry)
+        # the 8-bit TN products (roofline: the fp8 MFMA peak)
+        from workloads import F8_WORKLOADS
+        for name, wf in F8_WORKLOADS.items():
+            ms_f, kms_f = time_f8_workload(tdg, torch, wf, max(20, args.steps), args.warmup)
+            also.append({"workload": name, "value": round(wf.flops / (ms_f * 1e-3) / 1e12, 2),
+                         "kernel_tflops": round(wf.flops / (kms_f * 1e-3) / 1e12, 2),
+                         "frac": round(wf.flops / (kms_f * 1e-3) / 1e12 / PEAK_TFLOPS[wf.a_fmt], 4),
+                         "ms_per_step": round(ms_f, 5), "kernel_ms": round(kms_f, 5),
+                         "dtype": wf.a_fmt, "out_dtype": wf.out_dtype,
+                         "scales": ("E8M0 per 32-element K block" if wf.block_scales else "none") +
+                                   (" + fp32 per row" if wf.row_scales else "")})
         line["also"] = also
     if not args.no_gpu_state:
         line["gpu_state"] = gpu_state_under_load(tdg, torch, w, kernel_ms)

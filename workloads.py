@@ -144,3 +144,37 @@ def make_f8_inputs(M: int, N: int, K: int, a_fmt: str = "e4m3", b_fmt: str = "e4
         sa = (torch.rand((M,), generator=gen) * 1.5 + 0.5).numpy()
         sb = (torch.rand((N,), generator=gen) * 1.5 + 0.5).numpy()
     return a, b, xa, xb, sa, sb
+
+
+@dataclass(frozen=True)
+class F8Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    a_fmt: str           # "e4m3" | "e5m2"
+    b_fmt: str
+    out_dtype: str       # "f16" | "bf16" | "f32"
+    block_scales: bool   # E8M0 scales per row and 32-element K block
+    row_scales: bool     # fp32 scales per row of A and of B
+    dist: str
+    seed: int
+    spread: int = 4
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# 8-bit TN products (C = A B^T with scales), measured beside the 16-bit ones.
+F8_WORKLOADS = {
+    "tn_e4m3_8192_blockscaled": F8Workload("tn_e4m3_8192_blockscaled", 8192, 8192, 8192, "e4m3", "e4m3", "bf16",
+                                           True, True, "normal", 83),
+    "tn_e4m3_8192": F8Workload("tn_e4m3_8192", 8192, 8192, 8192, "e4m3", "e4m3", "bf16", False, False,
+                               "normal", 84),
+}
+
+
+def f8_workload_inputs(w: F8Workload):
+    return make_f8_inputs(w.M, w.N, w.K, w.a_fmt, w.b_fmt, w.dist, w.seed, block_scales=w.block_scales,
+                          spread=w.spread, row_scales=w.row_scales)
