@@ -245,18 +245,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
 #pragma unroll
     for (int e = 0; e < NPR; ++e) sc[e] = 0x7f7f7f7f;   // every byte: scale 1
 
-    // The block-scale operands of K tile kt, read at the start of its
-    // iteration.  Blocks past the end of K (in the last tile) get scale 1
-    // -- their operands are zero, and those bytes are not part of the
-    // caller's scale rows -- as does an operand without block scales.
+    // The block-scale operands of K tile kt: read from LDS with the last
+    // slice of the previous iteration (or after the first barrier), packed
+    // at the start of the tile's iteration.  Blocks past the end of K (in
+    // the last tile) get scale 1 -- their operands are zero, and those bytes
+    // are not part of the caller's scale rows -- as does an operand without
+    // block scales.
     const bool has_xa = p.xa != nullptr, has_xb = p.xb != nullptr;
     const uint32_t perm_sel = 0x06020400u + 0x01010101u * (uint32_t)fg;
-    auto scales_for = [&](int kt) {
+    uint32_t raw[BSCALE ? RM + RN : 1];
+    auto scale_read = [&](int kt) {
         if constexpr (BSCALE) {
             const uint32_t *sg = scale_ptr(kt);
-            uint32_t raw[RM + RN];
 #pragma unroll
             for (int e = 0; e < RM + RN; ++e) raw[e] = e < RM ? sg[sa_w + 128 * e] : sg[sb_w + 128 * (e - RM)];
+        }
+    };
+    auto scales_for = [&](int kt) {
+        if constexpr (BSCALE) {
             // (uniform masks of the bytes to keep: one bit-field insert each)
             const int rem = nkb - 4 * kt;
             const uint32_t keep = rem >= 4 ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << (8 * rem)) - 1u));
@@ -279,6 +285,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         static_for<0, NFR>([&](auto d) { frag_op(d, smem, 0, al[0], ah[0], bl[0], bh[0]); });
+        scale_read(0);
     }
 
     // One K tile per iteration, as in the 16-bit kernel: step 0's MFMAs with
@@ -314,6 +321,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
             static_for<s0 * NFR / NSUB, (s0 + 1) * NFR / NSUB>(
                 [&](auto d) { frag_op(d, nxt, 0, al[0], ah[0], bl[0], bh[0]); });
             if constexpr (s0 == 0) scale_group(kt + STAGES);
+            if constexpr (s0 == NSUB - 1) scale_read(kt + 1);
             dma_op(sub, kt + STAGES, cur);
             __builtin_amdgcn_sched_barrier(0);
         });
