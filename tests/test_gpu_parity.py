@@ -474,3 +474,36 @@ def test_autotune_transposed_operands(tdg):
     torch.cuda.synchronize()
     check_exact(out.cpu(), ref_gemm(a, b, "bf16", "nn"), "f32", "autotuned storage")
     tdg.tdg_autotune_clear()
+
+
+# ---------------------------------------------------------------------------
+# Persistent form of the 16x16x32 kernel: workgroups walking several tiles
+# ---------------------------------------------------------------------------
+
+# (layout, M, N, K, batch): more 256 x 256 tiles than CUs, so workgroups take
+# two or more tiles; ragged M, N and K tails; K = 64 (one K tile: the loads
+# run ahead across several tiles); a batch whose tiles switch problems.
+PERSISTENT_SHAPES = [("tn", 4347, 4349, 200, 0), ("nn", 4352, 4344, 64, 0), ("tn", 2048, 2048, 72, 5),
+                     ("nn", 4360, 4096, 136, 0)]
+
+
+@pytest.mark.parametrize("layout,M,N,K,batch", PERSISTENT_SHAPES)
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_persistent_kernel_integer_exact(tdg, layout, M, N, K, batch, out_dtype):
+    cfg = [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i).endswith("_m16p")][0]
+    announce("persistent", layout, M, N, K, batch, out_dtype)
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M + N + K + batch, batch=batch)
+    c = gpu_gemm(tdg, a, b, layout, out_dtype, config=cfg)
+    check_exact(c, ref_gemm(a, b, "bf16", layout), out_dtype, "persistent %s %dx%dx%d b%d" % (layout, M, N, K, batch))
+
+
+def test_persistent_kernel_random_and_repeatable(tdg):
+    cfg = [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i).endswith("_m16p")][0]
+    M, N, K = 4352, 4608, 1000
+    announce("persistent random", M, N, K)
+    a, b = make_inputs(M, N, K, "tn", "f16", "normal_k", seed=91)
+    c1 = gpu_gemm(tdg, a, b, "tn", "f16", config=cfg)
+    c2 = gpu_gemm(tdg, a, b, "tn", "f16", config=cfg)
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    rows = sample_rows(M)
+    check_tol(c1[torch.from_numpy(rows)], ref_gemm(a, b, "f16", "tn", rows=rows), "f16", K, "persistent random")

@@ -50,7 +50,8 @@ struct F8Args {
 // tiles of BK and ST pipeline stages; KIND 0 = the register-staged kernel
 // (BK 64, two stages), VEC = vectorised loads (aligned operands) or the
 // predicated element-load path (any operands); KIND 2 = the direct-to-LDS
-// kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64).
+// kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64); KIND 3 = its
+// persistent form (one workgroup per CU walking its tiles, K > 0).
 #define TDG_CONFIG_LIST(X)                                                   \
     X(0, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
     X(1, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
@@ -65,7 +66,8 @@ struct F8Args {
     X(10, 2, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16")          \
     X(11, 2, 128, 128, 64, 4, 2, 2, true, "128x128x64_s4_w2x2_m16")          \
     X(12, 2, 128, 128, 64, 4, 2, 4, true, "128x128x64_s4_w2x4_m16")          \
-    X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")
+    X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")          \
+    X(14, 3, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16p")
 
 // 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
 #define TDG_F8_CONFIG_LIST(X)                                   \

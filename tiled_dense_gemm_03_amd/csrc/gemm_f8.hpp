@@ -384,6 +384,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
                 const uint32_t off = row_ok ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
                 if constexpr (CT == OUT_F32) {
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                    store_data_read(v);
                 } else {
                     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                     u32x2 w;
@@ -399,6 +400,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
                                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
                     }
                     __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                    store_data_read(w);
                 }
             } else {
 #pragma unroll
@@ -407,11 +409,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
                     if constexpr (CT == OUT_F32) {
                         // (the words of the whole vector: hipcc's bit cast of a
                         // single vector element reads element 0 whatever the index)
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32x4, v)[r], rc, off, 0, 0);
+                        const uint32_t x = __builtin_bit_cast(u32x4, v)[r];
+                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, 0);
+                        store_data_read(x);
                     } else if constexpr (CT == OUT_F16) {
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v[r]), rc, off, 0, 0);
+                        const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        store_data_read(x);
                     } else {
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v[r]), rc, off, 0, 0);
+                        const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        store_data_read(x);
                     }
                 }
             }

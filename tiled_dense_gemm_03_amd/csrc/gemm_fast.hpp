@@ -462,6 +462,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
                 const int cn = wave_n * WTN + chunk * 16 / ES;
                 const uint32_t off = (m0 + cm < M) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
                 __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
+                store_data_read(w);
             }
         }
     } else {
@@ -478,11 +479,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
                     const uint32_t off = (row_ok && n0 + cn < N) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
                     const float v = acc[i][j][r];
                     if constexpr (CT == OUT_F32) {
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, off, 0, 0);
+                        const uint32_t x = __builtin_bit_cast(uint32_t, v);
+                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, 0);
+                        store_data_read(x);
                     } else if constexpr (CT == OUT_F16) {
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), rc, off, 0, 0);
+                        const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        store_data_read(x);
                     } else {
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), rc, off, 0, 0);
+                        const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        store_data_read(x);
                     }
                 }
             }

@@ -4,6 +4,7 @@
 #include "gemm_fast.hpp"
 #include "gemm_kernel.hpp"
 #include "gemm_m16.hpp"
+#include "gemm_m16p.hpp"
 
 #ifndef TDG_TRANSB
 #error "TDG_TRANSB must be defined"
@@ -23,6 +24,10 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
         static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
         hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
+    } else if constexpr (KIND == 3) {
+        static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
+        hipLaunchKernelGGL((gemm_m16p_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT>), dim3((unsigned)grid),
+                           dim3(WM * WN * 64), 0, s, a);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TB, TDG_AB, CT, VEC>), dim3((unsigned)grid),
                            dim3(NTHREADS), 0, s, a);
@@ -32,7 +37,7 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
 template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TA, bool VEC>
 static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     constexpr bool TB = TDG_TRANSB != 0;
-    if constexpr ((KIND >= 1 && !TB && BN / 8 < 16) || (TA && (KIND != 2 || BM / 8 < 16))) {
+    if constexpr ((KIND >= 1 && !TB && BN / 8 < 16) || (TA && (KIND < 2 || BM / 8 < 16))) {
         return hipErrorInvalidValue;   // an MC operand needs the direct-to-LDS kernels with >= 128-wide rows
     } else {
         switch (ct) {

@@ -82,14 +82,31 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int lim) {
     return v;
 }
 
+// Called right after a store to global memory with the store's data: keeps
+// those registers unchanged until the store has read them (s_waitcnt
+// expcnt(0)).  hipcc reuses a store's data registers for the next value as
+// soon as the store is issued, and on gfx950 a register write that closely
+// follows a store has been seen to reach the store's data (wrong output
+// elements, nondeterministically, in an epilogue that stored straight from
+// registers); every epilogue store of the library goes through this.
+template <class T>
+__device__ __forceinline__ void store_data_read(const T &x) {
+    asm volatile("s_waitcnt expcnt(0)" ::"v"(x));
+}
+
 template <int CT>
 __device__ __forceinline__ void store_out(void *C, int64_t off, float v) {
     if constexpr (CT == OUT_F32) {
         reinterpret_cast<float *>(C)[off] = v;
+        store_data_read(v);
     } else if constexpr (CT == OUT_F16) {
-        reinterpret_cast<_Float16 *>(C)[off] = (_Float16)v;
+        const _Float16 h = (_Float16)v;
+        reinterpret_cast<_Float16 *>(C)[off] = h;
+        store_data_read(h);
     } else {
-        reinterpret_cast<__bf16 *>(C)[off] = (__bf16)v;
+        const __bf16 h = (__bf16)v;
+        reinterpret_cast<__bf16 *>(C)[off] = h;
+        store_data_read(h);
     }
 }
 

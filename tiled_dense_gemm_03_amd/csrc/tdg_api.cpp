@@ -186,7 +186,8 @@ bool split_pays(const SplitPlan &pl, int64_t cus) {
 
 // Tile-configuration choice (measured on MI355X), with `cus` the device's
 // compute units: 256 x 256 tiles on the 16 x 16 x 32 MFMA kernel when the
-// problem has at least one such tile per CU; 128 x 128 tiles on the same
+// problem has at least one such tile per CU (its persistent form for TN
+// products of several rounds with 16-bit output); 128 x 128 tiles on the same
 // kernel (8 waves, 4 stages) for smaller problems; the 32 x 32 x 16 direct
 // load kernel or the register-staged kernel when the 16 x 16 x 32 kernel
 // cannot address the operands; the predicated kernel for misaligned
@@ -198,6 +199,13 @@ int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t batch
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
+        // several rounds of K-contiguous operands with 16-bit output: the
+        // persistent form (measured +5% on 8192^3 TN; no gain on NN, where
+        // the NN-B loads are less latency-bound, nor in a single round)
+        const int pid = config_by_name("256x256x64_s2_w2x4_m16p");
+        if (tiles256 >= 2 * cus && transb && !transa && c_type != TDG_F32 &&
+            config_ok(kConfigs[pid], transa, transb, vec, lda, ldb, ldc, c_type))
+            return pid;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
         if (tiles256 >= cus && config_ok(kConfigs[id], transa, transb, vec, lda, ldb, ldc, c_type)) return id;
         const int mid = config_by_name("128x128x64_s4_w2x4_m16");
@@ -268,6 +276,29 @@ tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int6
     a.tiles_n = (int)cdiv(N, cf.bn);
     a.tiles_per_batch = a.tiles_m * a.tiles_n;
     const int64_t tiles = (int64_t)a.tiles_per_batch * batch;
+    if (cf.kind == 3) {
+        // persistent: one workgroup per CU (its LDS stages take most of a CU),
+        // each walking tiles w, w + grid, ...; a K of 0 (nothing to walk) is
+        // served by the one-tile-per-workgroup kernel of the same tiles
+        if (K == 0)
+            return launch(config_by_name("256x256x64_s2_w2x4_m16"), transa, transb, M, N, K, A, lda, sA, B, ldb, sB, C,
+                          ldc, sC, batch, ab_type, c_type, stream, nullptr, 0, cus);
+        a.ws = nullptr;
+        a.ws_flags = nullptr;
+        a.dp_tiles = (int)tiles;
+        a.sk_split = 1;
+        const int64_t grid = tiles < cus ? tiles : cus;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        hipError_t e;
+        if (transb == 0)
+            e = (ab_type == TDG_F16) ? launch_t0_ab0(config, c_type, transa, a, grid, s)
+                                     : launch_t0_ab1(config, c_type, transa, a, grid, s);
+        else
+            e = (ab_type == TDG_F16) ? launch_t1_ab0(config, c_type, transa, a, grid, s)
+                                     : launch_t1_ab1(config, c_type, transa, a, grid, s);
+        if (e != hipSuccess) return fail(TDG_LAUNCH_FAILED, "kernel launch failed: %s", hipGetErrorString(e));
+        return TDG_SUCCESS;
+    }
     SplitPlan pl{tiles, 0, 1};
     if (cf.kind == 2 && ws != nullptr) {
         pl = plan_split(tiles, cdiv(K, cf.bk), cus);
@@ -423,7 +454,7 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
     // Automatic choice on a single problem with a partial last round of
     // 256 x 256 tiles: whole rounds on one band of C, 128 x 128 tiles on the
     // rest (two launches on the stream, disjoint parts of C).
-    if (automatic && !tuned && cf.kind == 2 && batch == 1) {
+    if (automatic && !tuned && cf.kind >= 2 && batch == 1) {
         const int small = config_by_name("128x128x64_s4_w2x4_m16");
         bool cols = true;
         const int64_t cut = plan_retile(M, N, cus, &cols);
