@@ -255,6 +255,14 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5)},
     }
+    es = 4 if w.out_dtype == "f32" else 2
+    alg_bytes = (2 * (w.M * w.K + w.K * w.N) + es * w.M * w.N) * max(1, w.batch)
+    if flops / alg_bytes < peak / HBM_GBPS * 1e3:
+        # below the ridge point: the kernel is bounded by HBM bytes, not FLOPs
+        gbps = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        line["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                            "frac": round(gbps / HBM_GBPS, 4), "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
+                            "tflops": round(achieved, 2)}
     if not args.no_also:
         # the other measured workloads: the 4096^3 product of the metric, the
         # ragged single product and the HBM-bound batched TN product (whose
