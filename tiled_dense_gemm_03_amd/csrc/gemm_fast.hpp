@@ -461,7 +461,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
                 const int cm = wave_m * WTM + i * 32 + row;
                 const int cn = wave_n * WTN + chunk * 16 / ES;
                 const uint32_t off = (m0 + cm < M) ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
-                __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, 0, STORE_NT);
                 store_data_read(w);
             }
         }
@@ -480,15 +480,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fast_kernel(GemmArgs p) {
                     const float v = acc[i][j][r];
                     if constexpr (CT == OUT_F32) {
                         const uint32_t x = __builtin_bit_cast(uint32_t, v);
-                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     } else if constexpr (CT == OUT_F16) {
                         const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     } else {
                         const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     }
                 }

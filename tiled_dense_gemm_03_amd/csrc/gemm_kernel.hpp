@@ -82,6 +82,12 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int lim) {
     return v;
 }
 
+// Cache policy of the output stores: non-temporal (the "nt" bit of gfx950's
+// buffer stores).  C is written once and never read back by the kernel;
+// streaming it past the caches raised the HBM-bound batched TN product with
+// fp32 output from 4.38 to 5.36 TB/s (same process, interleaved timing).
+constexpr int STORE_NT = 2;
+
 // Called right after a store to global memory with the store's data: keeps
 // those registers unchanged until the store has read them (s_waitcnt
 // expcnt(0)).  hipcc reuses a store's data registers for the next value as
@@ -97,15 +103,15 @@ __device__ __forceinline__ void store_data_read(const T &x) {
 template <int CT>
 __device__ __forceinline__ void store_out(void *C, int64_t off, float v) {
     if constexpr (CT == OUT_F32) {
-        reinterpret_cast<float *>(C)[off] = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<float *>(C) + off);
         store_data_read(v);
     } else if constexpr (CT == OUT_F16) {
         const _Float16 h = (_Float16)v;
-        reinterpret_cast<_Float16 *>(C)[off] = h;
+        __builtin_nontemporal_store(h, reinterpret_cast<_Float16 *>(C) + off);
         store_data_read(h);
     } else {
         const __bf16 h = (__bf16)v;
-        reinterpret_cast<__bf16 *>(C)[off] = h;
+        __builtin_nontemporal_store(h, reinterpret_cast<__bf16 *>(C) + off);
         store_data_read(h);
     }
 }

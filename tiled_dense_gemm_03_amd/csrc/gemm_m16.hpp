@@ -445,7 +445,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
             if (vec_store) {
                 const uint32_t off = row_ok ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
                 if constexpr (CT == OUT_F32) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, STORE_NT);
                     store_data_read(v);
                 } else {
                     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
                         w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
                     }
-                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, STORE_NT);
                     store_data_read(w);
                 }
             } else {
@@ -472,15 +472,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
                         // (the words of the whole vector: hipcc's bit cast of a
                         // single vector element reads element 0 whatever the index)
                         const uint32_t x = __builtin_bit_cast(u32x4, v)[r];
-                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     } else if constexpr (CT == OUT_F16) {
                         const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     } else {
                         const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
                         store_data_read(x);
                     }
                 }

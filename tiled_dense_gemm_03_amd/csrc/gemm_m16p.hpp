@@ -256,7 +256,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                 const f32x4 v = acc[i][j];
                 if (vec_store) {
                     if constexpr (CT == OUT_F32) {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, vo, so, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, vo, so, STORE_NT);
                         store_data_read(v);
                     } else {
                         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -283,15 +283,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                             // (the words of the whole vector: hipcc's bit cast of a
                             // single vector element reads element 0 whatever the index)
                             const uint32_t x = __builtin_bit_cast(u32x4, v)[e];
-                            __builtin_amdgcn_raw_buffer_store_b32(x, rc, voe, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(x, rc, voe, so, STORE_NT);
                             store_data_read(x);
                         } else if constexpr (CT == OUT_F16) {
                             const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[e]);
-                            __builtin_amdgcn_raw_buffer_store_b16(x, rc, voe, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b16(x, rc, voe, so, STORE_NT);
                             store_data_read(x);
                         } else {
                             const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-                            __builtin_amdgcn_raw_buffer_store_b16(x, rc, voe, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b16(x, rc, voe, so, STORE_NT);
                             store_data_read(x);
                         }
                     }
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                         const int row = t * RPI + lane / CPR, piece = lane % CPR;
                         const u32x4 w = *reinterpret_cast<const u32x4 *>(stage_r + row * SROW + piece * 16);
                         const uint32_t off = row < rows_left ? (uint32_t)(row * p.ldc + piece * 8) * ES : OOB_OFFSET;
-                        __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, so_row, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(w, rc, off, so_row, STORE_NT);
                         store_data_read(w);
                     }
                 }
