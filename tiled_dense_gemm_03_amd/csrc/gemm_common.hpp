@@ -67,7 +67,8 @@ struct F8Args {
     X(11, 2, 128, 128, 64, 4, 2, 2, true, "128x128x64_s4_w2x2_m16")          \
     X(12, 2, 128, 128, 64, 4, 2, 4, true, "128x128x64_s4_w2x4_m16")          \
     X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")          \
-    X(14, 3, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16p")
+    X(14, 3, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16p")         \
+    X(15, 2, 256, 256, 64, 2, 2, 2, true, "256x256x64_s2_w2x2_m16")
 
 // 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
 #define TDG_F8_CONFIG_LIST(X)                                   \

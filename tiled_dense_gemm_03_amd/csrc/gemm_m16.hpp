@@ -58,6 +58,41 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     }
 }
 
+// The same MFMA as inline assembly with the accumulator tied to AccVGPRs
+// (the "+a" operand is both source C and destination).  Used when a wave's
+// accumulators outgrow the VGPRs: hipcc then mixes register classes for the
+// intrinsic and copies accumulators between them on every K step.  The
+// compiler does not know the statement is an MFMA, so its users (i) order
+// it by hand (sched_barrier; IGroupLP cannot classify it), (ii) wait out the
+// MFMA result latency before any other instruction reads an accumulator
+// (mfma_asm_drain) and (iii) keep the zero initialisation of the
+// accumulators apart from the first MFMA (mfma_asm_pin).
+template <int AB>
+__device__ __forceinline__ f32x4 mfma_16x16x32_acc(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (AB == AB_F16) {
+        asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    } else {
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    }
+    return c;
+}
+__device__ __forceinline__ void mfma_asm_pin(f32x4 &c) { asm volatile("" : "+a"(c)); }
+
+// Direct 16-byte load to LDS address lds_base + IMM with M0 as an operand of
+// the statement (one scalar move per load instead of saving and restoring
+// M0 around it).
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16_m0(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base + IMM) : "memory");
+}
+template <bool M0_OPERAND, uint32_t IMM>
+__device__ __forceinline__ void dma16_sel(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+    if constexpr (M0_OPERAND) dma16_m0<IMM>(rsrc, voff, lds_base);
+    else dma16<IMM>(rsrc, voff, lds_base);
+}
+// 32 wait states: more than the 8-pass MFMA's result latency for any reader.
+__device__ __forceinline__ void mfma_asm_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
 // Buffer descriptor words with an explicit record count (bytes).
 __device__ __forceinline__ u32x4 rsrc_words_n(const void *base, uint32_t records) {
     const uint64_t a = (uint64_t)base;
@@ -106,6 +141,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     constexpr int RPB = 64 / BNG, RPA = 64 / BMG;
     constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
     constexpr int NVA = !TRANSA ? 1 : 16 / ((NW * RPA) % 16 == 0 ? 16 : ((NW * RPA) % 8 == 0 ? 8 : ((NW * RPA) % 4 == 0 ? 4 : ((NW * RPA) % 2 == 0 ? 2 : 1))));
+
+    // Accumulators beyond 160 registers per lane (a 4-wave 128 x 128 wave
+    // tile has 256) are kept in AccVGPRs by the tied inline-assembly MFMA.
+    constexpr bool ASM_ACC = (BM / WM / 16) * (BN / WN / 16) * 4 > 160;
 
     __shared__ u32x4 smem[STAGES * STAGE];
     __shared__ int sk_last;
@@ -203,24 +242,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
             if constexpr (!TRANSA) {
                 const u32x4 rs = rsrc_words_n(Atile + k0, records_of((int64_t)(a_rows - 1) * lda + K - k0));
                 const uint32_t off = (k0 < kc_klim ? a_lane[0] : OOB_OFFSET) + (uint32_t)q * a_qs;
-                dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+                dma16_sel<ASM_ACC, (uint32_t)(q * NW) * 1024u>(rs, off, base);
             } else {
                 const u32x4 rs = rsrc_words_n(Atile + (int64_t)k0 * lda,
                                               records_of((int64_t)(K - k0 - 1) * lda + (M - m0)));
                 const uint32_t off = a_lane[q % NVA] + (uint32_t)q * a_qs;
-                dma16<(uint32_t)(q * NW) * 1024u>(rs, off, base);
+                dma16_sel<ASM_ACC, (uint32_t)(q * NW) * 1024u>(rs, off, base);
             }
         } else {
             constexpr int qb = q - QA;
             if constexpr (TRANSB) {
                 const u32x4 rs = rsrc_words_n(Btile + k0, records_of((int64_t)(b_rows - 1) * ldb + K - k0));
                 const uint32_t off = (k0 < kc_klim ? b_lane[0] : OOB_OFFSET) + (uint32_t)qb * b_qs;
-                dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
+                dma16_sel<ASM_ACC, (uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
             } else {
                 const u32x4 rs = rsrc_words_n(Btile + (int64_t)k0 * ldb,
                                               records_of((int64_t)(K - k0 - 1) * ldb + (N - n0)));
                 const uint32_t off = b_lane[qb % NVB] + (uint32_t)qb * b_qs;
-                dma16<(uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
+                dma16_sel<ASM_ACC, (uint32_t)(A_SLOTS * 16 + qb * NW * 1024)>(rs, off, base);
             }
         }
     };
@@ -298,7 +337,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
-        for (int j = 0; j < RN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < RN; ++j) {
+            acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (ASM_ACC) mfma_asm_pin(acc[i][j]);
+        }
 
     u32x4 af[2][RM], bf[2][RN];
 
@@ -316,32 +358,75 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // of stage s_cur.  The stage is a run-time index (one loop body, no
     // per-stage copies of the code).
     int s_cur = 0;
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
-        u32x4 *cur = smem + s_cur * STAGE;
-        u32x4 *nxt = smem + s_nxt * STAGE;
-        frags_from(cur, 1, af[1], bf[1]);
+    if constexpr (!ASM_ACC) {
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
+            u32x4 *cur = smem + s_cur * STAGE;
+            u32x4 *nxt = smem + s_nxt * STAGE;
+            frags_from(cur, 1, af[1], bf[1]);
 #pragma unroll
-        for (int i = 0; i < RM; ++i)
+            for (int i = 0; i < RM; ++i)
 #pragma unroll
-            for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[0][j], af[0][i], acc[i][j]);
-        interleave_hint<NMF, NDS>();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        wait_vm_lgkm0<(STAGES - 2) * NDMA>();
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        constexpr int NSUB = NDMA;
-        static_for<0, NSUB>([&](auto sub) {
-            constexpr int s0 = decltype(sub)::value;
-            static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
-                constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
-                acc[i][j] = mfma_16x16x32<AB>(bf[1][j], af[1][i], acc[i][j]);
+                for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[0][j], af[0][i], acc[i][j]);
+            interleave_hint<NMF, NDS>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vm_lgkm0<(STAGES - 2) * NDMA>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int NSUB = NDMA;
+            static_for<0, NSUB>([&](auto sub) {
+                constexpr int s0 = decltype(sub)::value;
+                static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
+                    constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                    acc[i][j] = mfma_16x16x32<AB>(bf[1][j], af[1][i], acc[i][j]);
+                });
+                static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>([&](auto d) { frag_op(d, nxt, 0, af[0], bf[0]); });
+                dma_op(sub, kt + STAGES, cur);
+                __builtin_amdgcn_sched_barrier(0);
             });
-            static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>([&](auto d) { frag_op(d, nxt, 0, af[0], bf[0]); });
-            dma_op(sub, kt + STAGES, cur);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        s_cur = s_nxt;
+            s_cur = s_nxt;
+        }
+    } else {
+        // The same schedule with every slice fenced by sched_barrier.  The
+        // fragment reads go in the order the MFMAs consume them (A fragment
+        // 0, every B fragment, then A fragments 1..), so that the MFMAs of
+        // a step can start before all of its fragments have arrived.
+        constexpr int PA = DA / RM, NB = NDS - DA;
+        auto rd = [](auto ctag) {
+            constexpr int c = decltype(ctag)::value;
+            return std::integral_constant<int, (c < PA ? c : (c < PA + NB ? DA + (c - PA) : c - NB))>{};
+        };
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
+            u32x4 *cur = smem + s_cur * STAGE;
+            u32x4 *nxt = smem + s_nxt * STAGE;
+            static_for<0, NDS>([&](auto c) {
+                constexpr int c0 = decltype(c)::value;
+                static_for<c0 * NMF / NDS, (c0 + 1) * NMF / NDS>([&](auto m) {
+                    constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                    acc[i][j] = mfma_16x16x32_acc<AB>(bf[0][j], af[0][i], acc[i][j]);
+                });
+                frag_op(rd(c), cur, 1, af[1], bf[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vm_lgkm0<(STAGES - 2) * NDMA>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            constexpr int NSUB = NDMA > NDS ? NDMA : NDS;
+            static_for<0, NSUB>([&](auto sub) {
+                constexpr int s0 = decltype(sub)::value;
+                static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
+                    constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                    acc[i][j] = mfma_16x16x32_acc<AB>(bf[1][j], af[1][i], acc[i][j]);
+                });
+                static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>([&](auto c) { frag_op(rd(c), nxt, 0, af[0], bf[0]); });
+                static_for<s0 * NDMA / NSUB, (s0 + 1) * NDMA / NSUB>([&](auto q) { dma_op(q, kt + STAGES, cur); });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            s_cur = s_nxt;
+        }
+        mfma_asm_drain();
     }
     __builtin_amdgcn_s_waitcnt(0);
 
