@@ -11,8 +11,10 @@ before timing, and stay there.
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps; then K timed steps
 between two device synchronisations (wall clock -> ms_per_step and value),
-with a HIP event pair around every launch on the stream the kernel runs on
-(-> the kernel's average duration for the roofline figure).
+with a HIP event pair on the stream the kernel runs on around the K
+launches (-> the kernel's average launch duration for the roofline figure:
+the launches run back to back, so the span is their durations plus the
+small gaps between them).
 """
 import argparse
 import hashlib
@@ -55,7 +57,21 @@ def stored_traffic(workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_workload(tdg, torch, w, steps, warmup):
+def warm_up(torch, call, steps, min_seconds):
+    """`steps` untimed calls, then more until `min_seconds` of wall time
+    have passed (the engine clock needs tens of milliseconds of load to
+    settle after an idle spell, e.g. while the host generates inputs)."""
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+
+
+def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
     from workloads import TORCH_DTYPE, workload_inputs
     a, b = workload_inputs(w)
     dev = torch.device("cuda:0")
@@ -64,23 +80,21 @@ def time_workload(tdg, torch, w, steps, warmup):
     shape = (w.batch, w.M, w.N) if w.batch else (w.M, w.N)
     c = torch.empty(shape, dtype=out_dt, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        tdg.gemm(a, b, layout=w.layout, out=c)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    warm_up(torch, lambda: tdg.gemm(a, b, layout=w.layout, out=c), warmup, min_warm_s)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         tdg.gemm(a, b, layout=w.layout, out=c)
-        ev[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    kernel_ms = start.elapsed_time(end) / steps
     cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
     return wall * 1e3 / steps, kernel_ms, tdg.tdg_config_name(cfg)
 
 
-def time_f8_workload(tdg, torch, w, steps, warmup):
+def time_f8_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
     """As time_workload, for an 8-bit workload (block-scale rows padded to a
     16-byte multiple, as the library asks)."""
     import numpy as np
@@ -106,18 +120,16 @@ def time_f8_workload(tdg, torch, w, steps, warmup):
     def call():
         tdg.gemm_f8(ad, bd, a_fmt=w.a_fmt, b_fmt=w.b_fmt, block_scale_a=xad, block_scale_b=xbd, scale_a=sad,
                     scale_b=sbd, out=c)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    warm_up(torch, call, warmup, min_warm_s)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         call()
-        ev[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    kernel_ms = start.elapsed_time(end) / steps
     return wall * 1e3 / steps, kernel_ms
 
 
@@ -204,7 +216,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="nn_bf16_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
@@ -272,7 +284,7 @@ def main():
             if name == w.name:
                 continue
             wa = WORKLOADS[name]
-            ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup)
+            ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup, 0.2)
             entry = {"workload": name, "value": round(wa.flops / (ms_a * 1e-3) / 1e12, 2),
                      "kernel_tflops": round(wa.flops / (kms_a * 1e-3) / 1e12, 2),
                      "frac": round(wa.flops / (kms_a * 1e-3) / 1e12 / PEAK_TFLOPS[wa.in_dtype], 4),
@@ -286,7 +298,7 @@ def main():
         # the 8-bit TN products (roofline: the fp8 MFMA peak)
         from workloads import F8_WORKLOADS
         for name, wf in F8_WORKLOADS.items():
-            ms_f, kms_f = time_f8_workload(tdg, torch, wf, max(20, args.steps), args.warmup)
+            ms_f, kms_f = time_f8_workload(tdg, torch, wf, max(20, args.steps), args.warmup, 0.2)
             also.append({"workload": name, "value": round(wf.flops / (ms_f * 1e-3) / 1e12, 2),
                          "kernel_tflops": round(wf.flops / (kms_f * 1e-3) / 1e12, 2),
                          "frac": round(wf.flops / (kms_f * 1e-3) / 1e12 / PEAK_TFLOPS[wf.a_fmt], 4),
