@@ -100,6 +100,16 @@ __device__ __forceinline__ void store_data_read(const T &x) {
     asm volatile("s_waitcnt expcnt(0)" ::"v"(x));
 }
 
+// The same for a group of stores issued back to back: one wait, after which
+// the data registers of every store of the group may be reused (the empty
+// statements keep them live until the wait has passed).
+template <int N, class T>
+__device__ __forceinline__ void store_data_read_all(const T (&x)[N]) {
+    asm volatile("s_waitcnt expcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < N; ++t) asm volatile("" ::"v"(x[t]));
+}
+
 template <int CT>
 __device__ __forceinline__ void store_out(void *C, int64_t off, float v) {
     if constexpr (CT == OUT_F32) {

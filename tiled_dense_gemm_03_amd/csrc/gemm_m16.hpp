@@ -514,6 +514,56 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     char *const region = reinterpret_cast<char *>(smem) + wave * 16 * ROWB;
     const int wrow = lane & 15, wcol = 4 * (lane >> 4);
+    constexpr int NT = 16 / RPI;                   // read-back instructions per 16-row block
+    if (vec_store) {
+        // Whole row segments: a block's read-backs, then its stores back to
+        // back, then one wait for their data.
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < RM; ++i) {
+#pragma unroll
+            for (int j = 0; j < RN; ++j)
+                *reinterpret_cast<f32x4 *>(region + wrow * ROWB + (16 * j + wcol) * 4) = acc[i][j];
+            f32x4 v[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int row = t * RPI + lane / CPR, chunk = lane % CPR;
+                v[t] = *reinterpret_cast<const f32x4 *>(region + row * ROWB + chunk * 16);
+            }
+            if constexpr (CT == OUT_F32) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int row = t * RPI + lane / CPR, chunk = lane % CPR;
+                    const int cm = wave_m * WTM + i * 16 + row, cn = wave_n * WTN + chunk * 4;
+                    const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[t]), rc, off, 0, STORE_NT);
+                }
+                store_data_read_all(v);
+            } else {
+                u32x2 w[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int row = t * RPI + lane / CPR, chunk = lane % CPR;
+                    const int cm = wave_m * WTM + i * 16 + row, cn = wave_n * WTN + chunk * 4;
+                    const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
+                    if constexpr (CT == OUT_F16) {
+                        w[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][0]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][1]) << 16);
+                        w[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][2]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][3]) << 16);
+                    } else {
+                        w[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][0]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][1]) << 16);
+                        w[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][2]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][3]) << 16);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(w[t], rc, off, 0, STORE_NT);
+                }
+                store_data_read_all(w);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
@@ -521,53 +571,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
             *reinterpret_cast<f32x4 *>(region + wrow * ROWB + (16 * j + wcol) * 4) = acc[i][j];
         }
 #pragma unroll
-        for (int t = 0; t < 16 / RPI; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const int row = t * RPI + lane / CPR, chunk = lane % CPR;
             const f32x4 v = *reinterpret_cast<const f32x4 *>(region + row * ROWB + chunk * 16);
             const int cm = wave_m * WTM + i * 16 + row;
             const int cn = wave_n * WTN + chunk * 4;
             const bool row_ok = m0 + cm < M;
-            if (vec_store) {
-                const uint32_t off = row_ok ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
-                if constexpr (CT == OUT_F32) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, off, 0, STORE_NT);
-                    store_data_read(v);
-                } else {
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    u32x2 w;
-                    if constexpr (CT == OUT_F16) {
-                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
-                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
-                    } else {
-                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
-                    }
-                    __builtin_amdgcn_raw_buffer_store_b64(w, rc, off, 0, STORE_NT);
-                    store_data_read(w);
-                }
-            } else {
+            // element by element: the tile passes N, or C is not 4-byte aligned
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t off = (row_ok && n0 + cn + r < N) ? (uint32_t)(cm * p.ldc + cn + r) * ES : OOB_OFFSET;
-                    if constexpr (CT == OUT_F32) {
-                        // (the words of the whole vector: hipcc's bit cast of a
-                        // single vector element reads element 0 whatever the index)
-                        const uint32_t x = __builtin_bit_cast(u32x4, v)[r];
-                        __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, STORE_NT);
-                        store_data_read(x);
-                    } else if constexpr (CT == OUT_F16) {
-                        const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
-                        store_data_read(x);
-                    } else {
-                        const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
-                        store_data_read(x);
-                    }
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t off = (row_ok && n0 + cn + r < N) ? (uint32_t)(cm * p.ldc + cn + r) * ES : OOB_OFFSET;
+                if constexpr (CT == OUT_F32) {
+                    // (the words of the whole vector: hipcc's bit cast of a
+                    // single vector element reads element 0 whatever the index)
+                    const uint32_t x = __builtin_bit_cast(u32x4, v)[r];
+                    __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, STORE_NT);
+                    store_data_read(x);
+                } else if constexpr (CT == OUT_F16) {
+                    const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
+                    __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
+                    store_data_read(x);
+                } else {
+                    const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+                    __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
+                    store_data_read(x);
                 }
             }
         }

@@ -11,10 +11,10 @@
 //    running STAGES K tiles ahead cross into the next output tile: its
 //    first operand tiles arrive while the current tile's last MFMAs run,
 //    and no tile after the first waits for the full load latency.
-//  * The epilogue stores the accumulators straight from registers (lane l
-//    holds four consecutive columns of one row), without LDS staging, since
-//    the stages then already hold the next tile's operands; the stores of
-//    one tile drain while the next tile computes.
+//  * The epilogue runs between two K iterations, while the stages already
+//    hold the next tile's operands, so it goes through a small staging area
+//    of its own (per wave, 16 rows of 16-bit values or 8 rows of fp32); the
+//    stores of one tile drain while the next tile computes.
 //
 // The NineToothed primer's decomposition (s4: one program per output tile,
 // K as a loop in the program) is unchanged: a workgroup runs several
@@ -46,12 +46,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
     constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
     constexpr int NVA = !TRANSA ? 1 : 16 / ((NW * RPA) % 16 == 0 ? 16 : ((NW * RPA) % 8 == 0 ? 8 : ((NW * RPA) % 4 == 0 ? 4 : ((NW * RPA) % 2 == 0 ? 2 : 1))));
 
-    // 16-bit output: a per-wave staging area for one 16-row block of the
-    // wave's sub-tile, outside the stages (which hold the next tile's
-    // operands when the epilogue runs)
+    // A per-wave staging area outside the stages (which hold the next
+    // tile's operands when the epilogue runs): one 16-row block of the
+    // wave's sub-tile in 16-bit values, or half a block in fp32.
     constexpr int ES = (CT == OUT_F32) ? 4 : 2;
-    constexpr int SROW = WTN * 2 + 16;                       // staged row: 16-bit values, padded by 16 bytes
-    constexpr int STG = (CT == OUT_F32) ? 0 : NW * 16 * SROW / 16;
+    constexpr int SROW = WTN * ES + 16;                      // staged row, padded by 16 bytes
+    constexpr int SR = (CT == OUT_F32) ? 8 : 16;             // rows staged at a time
+    constexpr int STG = NW * SR * SROW / 16;
     static_assert((STAGE * STAGES + STG) * 16 <= 160 * 1024, "LDS budget");
     __shared__ u32x4 smem[STAGES * STAGE + STG];
 
@@ -224,18 +225,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
 
     // ---- epilogue of one output tile, from the accumulators ----
     // Lane l holds C[m][n .. n+3] for m = 16 i + l % 16, n = 16 j + 4 (l / 16)
-    // of the wave's sub-tile.  Interior tiles, 16-bit output: each 16-row
-    // block is converted (round to nearest even) into the wave's staging
-    // area and read back as 16-byte row pieces, so each store instruction
-    // writes whole 128-byte rows; fp32 output: one 16-byte store per lane
-    // and block.  A ragged right edge or an unaligned C takes element
-    // stores.  Rows past M are never stored.  Each store address is a
-    // per-lane offset plus a uniform one, so the epilogue keeps almost
-    // nothing live across the K loop.
+    // of the wave's sub-tile.  Interior tiles: each 16-row block (fp32:
+    // each half block) is converted (round to nearest even) into the wave's
+    // staging area and read back as 16-byte row pieces, so each store
+    // instruction writes whole row segments.  A ragged right edge or an
+    // unaligned C takes element stores.  Rows past M are never stored.
+    // Each store address is a per-lane offset plus a uniform one, so the
+    // epilogue keeps almost nothing live across the K loop.
     const bool c_aligned = (((uintptr_t)p.C | (uintptr_t)(p.ldc * ES) | (uintptr_t)(p.sC * ES)) & 3) == 0;
     const uint32_t lane_off = (uint32_t)(fr * p.ldc + 4 * fg) * ES;
-    char *const stage_r = reinterpret_cast<char *>(smem + STAGES * STAGE) + wave * 16 * SROW;
-    char *const stage_w = stage_r + fr * SROW;
+    char *const stage_r = reinterpret_cast<char *>(smem + STAGES * STAGE) + wave * SR * SROW;
+    char *const stage_w = stage_r + (fr % SR) * SROW;
     auto epilogue = [&](int r) {
         int batch, tm, tn;
         tile_of(p, w0 + r * G, batch, tm, tn);
@@ -256,8 +256,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                 const f32x4 v = acc[i][j];
                 if (vec_store) {
                     if constexpr (CT == OUT_F32) {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, vo, so, STORE_NT);
-                        store_data_read(v);
+                        // staged below, half a block at a time
                     } else {
                         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                         u32x2 w;
@@ -296,9 +295,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                         }
                     }
                 }
-                acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (CT != OUT_F32 || !vec_store) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            if constexpr (CT != OUT_F32) {
+            if constexpr (CT == OUT_F32) {
+                // rows 8 h .. 8 h + 7 of the block: written by the lanes that
+                // hold them, read back as 4 rows x 16 pieces per instruction
+                constexpr int CPR = WTN * 4 / 16, RPI = 64 / CPR, NT = SR / RPI;
+                static_assert(CPR * RPI == 64 && SR % RPI == 0, "row pieces must tile a wave");
+                if (vec_store) {
+#pragma unroll
+                    for (int h = 0; h < 16 / SR; ++h) {
+                        if (fr / SR == h) {
+#pragma unroll
+                            for (int j = 0; j < RN; ++j)
+                                *reinterpret_cast<f32x4 *>(stage_w + (16 * j + 4 * fg) * 4) = acc[i][j];
+                        }
+                        u32x4 w[NT];
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const int row = t * RPI + lane / CPR, piece = lane % CPR;
+                            w[t] = *reinterpret_cast<const u32x4 *>(stage_r + row * SROW + piece * 16);
+                        }
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const int row = h * SR + t * RPI + lane / CPR, piece = lane % CPR;
+                            const uint32_t off =
+                                row < rows_left ? (uint32_t)(row * p.ldc + piece * 4) * ES : OOB_OFFSET;
+                            __builtin_amdgcn_raw_buffer_store_b128(w[t], rc, off, so_row, STORE_NT);
+                        }
+                        store_data_read_all(w);
+                    }
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            } else {
                 // read back the 16 staged rows: 16-byte pieces, rows of the
                 // block t * RPI + lane / CPR, piece lane % CPR
                 constexpr int CPR = WTN * 2 / 16, RPI = 64 / CPR;
