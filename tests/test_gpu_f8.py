@@ -141,10 +141,11 @@ def test_f8_transposed_store_exact(tdg, config):
 
 
 def test_f8_k_edges_and_degenerate(tdg):
-    # K = 16: one partial K tile and a single block; K = 0: zeros
-    for K in (16, 48, 144, 272):
+    # K = 16: one partial K tile and a single block; K tails within a
+    # 32-element block and within a K tile; K = 0: zeros
+    for K in (16, 48, 144, 272, 400, 1040):
         announce("f8 K edge", K)
-        a, b, xa, xb, _, _ = make_f8_inputs(70, 90, K, "e4m3", "e5m2", "ints", 79 + K, block_scales=True, spread=1)
+        a, b, xa, xb, _, _ = make_f8_inputs(70, 290, K, "e4m3", "e5m2", "ints", 79 + K, block_scales=True, spread=1)
         c = gpu_f8(tdg, a, b, "e4m3", "e5m2", xa, xb, out="f32")
         check_exact(c, oracle.gemm_f8(a, b, "e4m3", "e5m2", xa=xa, xb=xb), "f32", "K=%d" % K)
     announce("f8 K=0")
