@@ -310,6 +310,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
         wait_vm_lgkm0<(STAGES - 2) * NDMA>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wave_priority<1>();
         constexpr int NSUB = NDMA;
         static_for<0, NSUB>([&](auto sub) {
             constexpr int s0 = decltype(sub)::value;
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f8_kernel(F8Args p) {
             dma_op(sub, kt + STAGES, cur);
             __builtin_amdgcn_sched_barrier(0);
         });
+        wave_priority<0>();
         s_cur = s_nxt;
     }
     __builtin_amdgcn_s_waitcnt(0);
