@@ -14,7 +14,10 @@ between two device synchronisations (wall clock -> ms_per_step and value),
 with a HIP event pair on the stream the kernel runs on around the K
 launches (-> the kernel's average launch duration for the roofline figure:
 the launches run back to back, so the span is their durations plus the
-small gaps between them).
+small gaps between them).  The other workloads are timed the same way over
+at least 50 ms of launches, five times, and report the medians; the
+HBM-bound batched product is also timed with the caches emptied before
+each launch.
 """
 import argparse
 import hashlib
@@ -71,7 +74,33 @@ def warm_up(torch, call, steps, min_seconds):
         torch.cuda.synchronize()
 
 
-def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
+def timed_runs(torch, call, stream, steps, repeats=1, min_total_s=0.0):
+    """(wall ms, kernel ms) per call: `steps` back-to-back calls between two
+    device synchronisations, with one HIP event pair on `stream` around them.
+    With min_total_s, the call count is raised until a run takes at least
+    that long (estimated from a first run); with repeats > 1 the run is
+    repeated and the medians are returned."""
+    import statistics
+
+    def run(n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(n):
+            call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n, start.elapsed_time(end) / n
+
+    n = steps
+    if min_total_s > 0:
+        _, k_ms = run(steps)
+        n = max(steps, int(min_total_s * 1e3 / max(k_ms, 1e-6)) + 1)
+    res = [run(n) for _ in range(repeats)]
+    return statistics.median(r[0] for r in res), statistics.median(r[1] for r in res)
+
+
+def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_total_s=0.0):
     from workloads import TORCH_DTYPE, workload_inputs
     a, b = workload_inputs(w)
     dev = torch.device("cuda:0")
@@ -80,21 +109,43 @@ def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
     shape = (w.batch, w.M, w.N) if w.batch else (w.M, w.N)
     c = torch.empty(shape, dtype=out_dt, device=dev)
     stream = torch.cuda.current_stream(dev)
-    warm_up(torch, lambda: tdg.gemm(a, b, layout=w.layout, out=c), warmup, min_warm_s)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
+
+    def call():
         tdg.gemm(a, b, layout=w.layout, out=c)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = start.elapsed_time(end) / steps
+    warm_up(torch, call, warmup, min_warm_s)
+    wall_ms, kernel_ms = timed_runs(torch, call, stream, steps, repeats, min_total_s)
     cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
-    return wall * 1e3 / steps, kernel_ms, tdg.tdg_config_name(cfg)
+    return wall_ms, kernel_ms, tdg.tdg_config_name(cfg)
 
 
-def time_f8_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
+def time_flushed(tdg, torch, w, reps=20):
+    """Median kernel duration of `w` with the L2 caches and the Infinity
+    Cache emptied of its operands before each launch: a 2 x 320 MiB device
+    copy (more than the 256 MiB Infinity Cache) runs between launches, and
+    an event pair on the stream brackets the launch alone."""
+    import statistics
+    from workloads import TORCH_DTYPE, workload_inputs
+    a, b = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    a, b = a.to(dev), b.to(dev)
+    shape = (w.batch, w.M, w.N) if w.batch else (w.M, w.N)
+    c = torch.empty(shape, dtype=TORCH_DTYPE[w.out_dtype], device=dev)
+    src = torch.ones(320 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps + 3):
+        dst.copy_(src)
+        if i >= 3:
+            ev[i - 3][0].record(stream)
+        tdg.gemm(a, b, layout=w.layout, out=c)
+        if i >= 3:
+            ev[i - 3][1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(s.elapsed_time(e) for s, e in ev)
+
+
+def time_f8_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_total_s=0.0):
     """As time_workload, for an 8-bit workload (block-scale rows padded to a
     16-byte multiple, as the library asks)."""
     import numpy as np
@@ -121,16 +172,7 @@ def time_f8_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0):
         tdg.gemm_f8(ad, bd, a_fmt=w.a_fmt, b_fmt=w.b_fmt, block_scale_a=xad, block_scale_b=xbd, scale_a=sad,
                     scale_b=sbd, out=c)
     warm_up(torch, call, warmup, min_warm_s)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        call()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = start.elapsed_time(end) / steps
-    return wall * 1e3 / steps, kernel_ms
+    return timed_runs(torch, call, stream, steps, repeats, min_total_s)
 
 
 def cpu_baseline(w, seconds_min=10.0):
@@ -284,7 +326,8 @@ def main():
             if name == w.name:
                 continue
             wa = WORKLOADS[name]
-            ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup, 0.2)
+            ms_a, kms_a, cfg_a = time_workload(tdg, torch, wa, max(20, args.steps), args.warmup, 0.2,
+                                               repeats=5, min_total_s=0.05)
             entry = {"workload": name, "value": round(wa.flops / (ms_a * 1e-3) / 1e12, 2),
                      "kernel_tflops": round(wa.flops / (kms_a * 1e-3) / 1e12, 2),
                      "frac": round(wa.flops / (kms_a * 1e-3) / 1e12 / PEAK_TFLOPS[wa.in_dtype], 4),
@@ -294,11 +337,19 @@ def main():
             if wa.flops / nbytes < PEAK_TFLOPS[wa.in_dtype] / HBM_GBPS * 1e3:
                 entry["hbm_gbps"] = round(nbytes / (kms_a * 1e-3) / 1e9, 1)
                 entry["hbm_frac"] = round(nbytes / (kms_a * 1e-3) / 1e9 / HBM_GBPS, 4)
+                # the inputs fit in the Infinity Cache: also with it emptied
+                kms_f = time_flushed(tdg, torch, wa)
+                entry["flushed"] = {"kernel_ms": round(kms_f, 5),
+                                    "hbm_gbps": round(nbytes / (kms_f * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(nbytes / (kms_f * 1e-3) / 1e9 / HBM_GBPS, 4),
+                                    "method": "2 x 320 MiB device copy before each launch; event pair "
+                                              "around the launch; median of 20"}
             also.append(entry)
         # the 8-bit TN products (roofline: the fp8 MFMA peak)
         from workloads import F8_WORKLOADS
         for name, wf in F8_WORKLOADS.items():
-            ms_f, kms_f = time_f8_workload(tdg, torch, wf, max(20, args.steps), args.warmup, 0.2)
+            ms_f, kms_f = time_f8_workload(tdg, torch, wf, max(20, args.steps), args.warmup, 0.2,
+                                           repeats=5, min_total_s=0.05)
             also.append({"workload": name, "value": round(wf.flops / (ms_f * 1e-3) / 1e12, 2),
                          "kernel_tflops": round(wf.flops / (kms_f * 1e-3) / 1e12, 2),
                          "frac": round(wf.flops / (kms_f * 1e-3) / 1e12 / PEAK_TFLOPS[wf.a_fmt], 4),
