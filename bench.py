@@ -344,6 +344,9 @@ def main():
                                     "hbm_frac": round(nbytes / (kms_f * 1e-3) / 1e9 / HBM_GBPS, 4),
                                     "method": "2 x 320 MiB device copy before each launch; event pair "
                                               "around the launch; median of 20"}
+            if not args.no_cpu_baseline:
+                # the oracle on the same workload (a bounded sample, as for the headline)
+                entry["cpu_baseline"] = cpu_baseline(wa, seconds_min=2.0)
             also.append(entry)
         # the 8-bit TN products (roofline: the fp8 MFMA peak)
         from workloads import F8_WORKLOADS
