@@ -509,13 +509,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 
     // ---- epilogue: fp32 -> output type, store mask of the primer's s5 ----
     // Lane l holds C[m][n] for m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
-    // One 16-row block of the wave's sub-tile at a time goes through the
-    // wave's own LDS region in fp32 (the accumulators are written as they
-    // are, so they never need to be copied out of the accumulator registers
-    // all at once); each lane then reads back 4 consecutive fp32 values of a
-    // row, converts them (round to nearest even) and stores them: whole row
-    // segments for interior tiles, element by element where the tile passes
-    // N or C is not 4-byte aligned.  Rows past M are never stored.
+    // Interior tiles go through LDS a band of whole tile rows at a time (see
+    // below) and are stored as complete rows.  Where the tile passes N or C
+    // is not 4-byte aligned, one 16-row block of the wave's sub-tile at a
+    // time goes through the wave's own LDS region in fp32; each lane reads
+    // back 4 consecutive values of a row, converts them (round to nearest
+    // even) and stores them element by element.  Rows past M are never
+    // stored.
     constexpr int ES = (CT == OUT_F32) ? 4 : 2;
     constexpr int ROWB = WTN * 4 + 16;             // staged row: fp32, padded by 16 bytes
     constexpr int CPR = WTN / 4;                   // 4-column chunks per row
@@ -531,51 +531,74 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     const int wrow = lane & 15, wcol = 4 * (lane >> 4);
     constexpr int NT = 16 / RPI;                   // read-back instructions per 16-row block
     if (vec_store) {
-        // Whole row segments: a block's read-backs, then its stores back to
-        // back, then one wait for their data.
+        // Interior tile: whole rows of the workgroup's tile at a time.  In
+        // pass p, the waves that hold rows p*PR .. p*PR + PR - 1 write them,
+        // converted to the output type, into LDS (row stride BN*ES + 16
+        // bytes); after a barrier every wave reads back whole tile rows
+        // (16 bytes per lane, LPR lanes per row) and stores them, so each
+        // store instruction writes one or more complete BN-wide rows of C.
+        constexpr int RS = BN * ES + 16;
+        constexpr int BUDGET = STAGES * STAGE * 16;
+        constexpr int PR = (WTM * RS <= BUDGET) ? WTM : (WTM / 2 * RS <= BUDGET) ? WTM / 2 : WTM / 4;
+        static_assert(PR % 16 == 0 && WTM % PR == 0 && PR * RS <= BUDGET, "epilogue pass fits in LDS");
+        constexpr int LPR = BN * ES / 16;                 // lanes per row
+        static_assert(64 % LPR == 0, "whole rows per store instruction");
+        constexpr int RPS = 64 / LPR;                     // rows per store instruction
+        static_assert(PR % (NW * RPS) == 0, "rows spread evenly over the waves");
+        constexpr int NST = PR / (NW * RPS);              // store instructions per wave and pass
+        char *const rows = reinterpret_cast<char *>(smem);
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int i = 0; i < RM; ++i) {
+        for (int pass = 0; pass < BM / PR; ++pass) {
+            constexpr int BPP = PR / 16;                  // 16-row blocks per pass
+            if (wave_m == pass * PR / WTM) {
+                const int i0 = (pass * PR % WTM) / 16;
 #pragma unroll
-            for (int j = 0; j < RN; ++j)
-                *reinterpret_cast<f32x4 *>(region + wrow * ROWB + (16 * j + wcol) * 4) = acc[i][j];
-            f32x4 v[NT];
+                for (int ib = 0; ib < BPP; ++ib) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int row = t * RPI + lane / CPR, chunk = lane % CPR;
-                v[t] = *reinterpret_cast<const f32x4 *>(region + row * ROWB + chunk * 16);
-            }
-            if constexpr (CT == OUT_F32) {
+                    for (int j = 0; j < RN; ++j) {
+                        // (i0 + ib) is uniform; select the block without
+                        // dynamic indexing of the accumulator array
+                        f32x4 v = acc[0][j];
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int row = t * RPI + lane / CPR, chunk = lane % CPR;
-                    const int cm = wave_m * WTM + i * 16 + row, cn = wave_n * WTN + chunk * 4;
-                    const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[t]), rc, off, 0, STORE_NT);
-                }
-                store_data_read_all(v);
-            } else {
-                u32x2 w[NT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int row = t * RPI + lane / CPR, chunk = lane % CPR;
-                    const int cm = wave_m * WTM + i * 16 + row, cn = wave_n * WTN + chunk * 4;
-                    const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc + cn) * ES : OOB_OFFSET;
-                    if constexpr (CT == OUT_F16) {
-                        w[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][0]) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][1]) << 16);
-                        w[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][2]) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[t][3]) << 16);
-                    } else {
-                        w[t][0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][0]) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][1]) << 16);
-                        w[t][1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][2]) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[t][3]) << 16);
+                        for (int i = 1; i < RM; ++i) if (i == i0 + ib) v = acc[i][j];
+                        char *dst = rows + (ib * 16 + wrow) * RS + (wave_n * WTN + 16 * j + wcol) * ES;
+                        if constexpr (CT == OUT_F32) {
+                            *reinterpret_cast<f32x4 *>(dst) = v;
+                        } else {
+                            u32x2 w;
+                            if constexpr (CT == OUT_F16) {
+                                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+                                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+                            } else {
+                                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+                                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+                            }
+                            *reinterpret_cast<u32x2 *>(dst) = w;
+                        }
                     }
-                    __builtin_amdgcn_raw_buffer_store_b64(w[t], rc, off, 0, STORE_NT);
                 }
-                store_data_read_all(w);
             }
+            __syncthreads();
+            u32x4 w[NST];
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int r = (wave * NST + t) * RPS + lane / LPR;
+                w[t] = *reinterpret_cast<const u32x4 *>(rows + r * RS + (lane % LPR) * 16);
+            }
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int r = (wave * NST + t) * RPS + lane / LPR;
+                const int cm = pass * PR + r;
+                const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc * ES + (lane % LPR) * 16) : OOB_OFFSET;
+                __builtin_amdgcn_raw_buffer_store_b128(w[t], rc, off, 0, STORE_NT);
+            }
+            store_data_read_all(w);
+            if (pass + 1 < BM / PR) __syncthreads();      // the rows are rewritten by the next pass
         }
         return;
     }
