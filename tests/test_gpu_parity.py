@@ -507,3 +507,39 @@ def test_persistent_kernel_random_and_repeatable(tdg):
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
     rows = sample_rows(M)
     check_tol(c1[torch.from_numpy(rows)], ref_gemm(a, b, "f16", "tn", rows=rows), "f16", K, "persistent random")
+
+
+# The 4-wave configuration (128 x 128 wave tiles, accumulators in AccVGPRs
+# through the tied inline-assembly MFMA): several tiles, ragged edges, long K,
+# both layouts and a batch whose tiles change problems.
+FOUR_WAVE_SHAPES = [("nn", 1000, 1304, 2056, 0), ("tn", 777, 1024, 1544, 0), ("tn", 512, 520, 4104, 3),
+                    ("nn", 256, 256, 64, 0)]
+
+
+def _four_wave_config(tdg):
+    return [i for i in range(tdg.tdg_num_configs()) if tdg.tdg_config_name(i) == "256x256x64_s2_w2x2_m16"][0]
+
+
+@pytest.mark.parametrize("layout,M,N,K,batch", FOUR_WAVE_SHAPES)
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f16"), ("bf16", "f32")])
+def test_four_wave_config_integer_exact(tdg, layout, M, N, K, batch, in_dtype, out_dtype):
+    cfg = _four_wave_config(tdg)
+    announce("4-wave", layout, M, N, K, batch, in_dtype, out_dtype)
+    a, b = make_inputs(M, N, K, layout, in_dtype, "ints", seed=M + 3 * N + K + batch, batch=batch)
+    c = gpu_gemm(tdg, a, b, layout, out_dtype, config=cfg)
+    check_exact(c, ref_gemm(a, b, in_dtype, layout), out_dtype, "4-wave %s %dx%dx%d b%d" % (layout, M, N, K, batch))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_four_wave_config_random_matches_default(tdg, layout):
+    """Random data: within tolerance of the oracle on sampled rows, and
+    repeatable launch to launch."""
+    cfg = _four_wave_config(tdg)
+    M, N, K = 1536, 1792, 3000
+    announce("4-wave random", layout, M, N, K)
+    a, b = make_inputs(M, N, K, layout, "bf16", "normal", seed=97)
+    c1 = gpu_gemm(tdg, a, b, layout, "bf16", config=cfg)
+    c2 = gpu_gemm(tdg, a, b, layout, "bf16", config=cfg)
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    rows = sample_rows(M)
+    check_tol(c1[torch.from_numpy(rows)], ref_gemm(a, b, "bf16", layout, rows=rows), "bf16", K, "4-wave random")
