@@ -6,15 +6,13 @@ variants bit for bit, every tile configuration on ragged shapes, strided
 operands, guard bands and NaN poison in padding, degenerate sizes and
 run-to-run determinism.
 """
-import math
 import sys
 
-import numpy as np
 import pytest
 import torch
 
-from parity import OUT_TORCH, check_exact, check_tol, ref_gemm, to_f64
-from workloads import WORKLOADS, bits, make_inputs, sample_rows, workload_inputs
+from parity import OUT_TORCH, check_exact, check_tol, ref_gemm
+from workloads import WORKLOADS, make_inputs, sample_rows, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
