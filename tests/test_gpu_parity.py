@@ -541,3 +541,33 @@ def test_four_wave_config_random_matches_default(tdg, layout):
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
     rows = sample_rows(M)
     check_tol(c1[torch.from_numpy(rows)], ref_gemm(a, b, "bf16", layout, rows=rows), "bf16", K, "4-wave random")
+
+
+# Leading dimensions so large that a 256-row (or 128-row) tile spans 2 GiB or
+# more: the direct-to-LDS kernels address a tile with 32-bit offsets, so the
+# library must pick a kernel that does not (checked on the host) and still
+# produce the exact result.  About 5 GB of device memory per operand.
+@pytest.mark.parametrize("which", ["lda", "ldc"])
+def test_leading_dimension_past_32_bit_offsets(tdg, which):
+    M, N, K = 300, 264, 136
+    big = (1 << 23) + 64                      # elements: 256 rows x big x 2 bytes > 2 GiB
+    announce("huge", which, big)
+    a, b = make_inputs(M, N, K, "nn", "f16", "ints", seed=123)
+    ref = ref_gemm(a, b, "f16", "nn")
+    if which == "lda":
+        buf = torch.zeros((M - 1) * big + K, dtype=torch.float16, device="cuda")
+        ad = torch.as_strided(buf, (M, K), (big, 1))
+        ad.copy_(a.cuda())
+        c = tdg.gemm(ad, b.cuda(), layout="nn", out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        check_exact(c.cpu(), ref, "f16", "huge lda")
+    else:
+        buf = torch.full(((M - 1) * big + N,), float("nan"), dtype=torch.float16, device="cuda")
+        cd = torch.as_strided(buf, (M, N), (big, 1))
+        tdg.gemm(a.cuda(), b.cuda(), layout="nn", out=cd)
+        torch.cuda.synchronize()
+        check_exact(cd.cpu(), ref, "f16", "huge ldc")
+        # nothing outside C was written: the first gap between rows 0 and 1
+        assert torch.isnan(buf[N:big].cpu()).all()
+    del buf
+    torch.cuda.empty_cache()
