@@ -571,3 +571,23 @@ def test_leading_dimension_past_32_bit_offsets(tdg, which):
         assert torch.isnan(buf[N:big].cpu()).all()
     del buf
     torch.cuda.empty_cache()
+
+
+def test_batch_stride_past_32_bit(tdg):
+    """Three TN problems whose A and C lie more than 2 GiB apart (batch
+    strides of 2^30 + 64 elements): exact results for every problem."""
+    batch, M, N, K = 3, 200, 264, 72
+    stride = (1 << 30) + 64
+    announce("huge batch stride", stride)
+    a, b = make_inputs(M, N, K, "tn", "bf16", "ints", seed=321, batch=batch)
+    ref = ref_gemm(a, b, "bf16", "tn")
+    abuf = torch.zeros((batch - 1) * stride + M * K, dtype=torch.bfloat16, device="cuda")
+    ad = torch.as_strided(abuf, (batch, M, K), (stride, K, 1))
+    ad.copy_(a.cuda())
+    cbuf = torch.full(((batch - 1) * stride + M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    cd = torch.as_strided(cbuf, (batch, M, N), (stride, N, 1))
+    tdg.gemm(ad, b.cuda(), layout="tn", out=cd)
+    torch.cuda.synchronize()
+    check_exact(cd.cpu(), ref, "f32", "huge batch stride")
+    del abuf, cbuf
+    torch.cuda.empty_cache()
