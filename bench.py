@@ -17,7 +17,11 @@ the launches run back to back, so the span is their durations plus the
 small gaps between them).  The other workloads are timed the same way over
 at least 50 ms of launches, five times, and report the medians; the
 HBM-bound batched product is also timed with the caches emptied before
-each launch.
+each launch.  "mfma_ceiling" is the rate of the bf16 kernel's MFMA stream
+with its operands in registers (libtdg_probe.so), on the headline's operand
+distribution and on zeros: the engine clock is power-limited and depends on
+the operand bits, so this, not the published peak, is what the MFMA-bound
+products can reach on random data.
 """
 import argparse
 import hashlib
@@ -224,6 +228,61 @@ def amd_smi_state():
         return None
 
 
+def mfma_ceiling(torch, seconds=0.25):
+    """Rate of the bf16 GEMM kernel's per-wave MFMA stream with its operands
+    held in registers (libtdg_probe.so, no memory traffic), one 8-wave
+    workgroup per CU, on N(0, 1) bf16 operands (the headline's inputs) and on
+    zeros: the practical ceiling of the MFMA-bound products at the clock the
+    board's power limit allows for those operand bits."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "tiled_dense_gemm_03_amd", "libtdg_probe.so"))
+    lib.tdgp_operand_elems.restype = ctypes.c_size_t
+    lib.tdgp_flops.restype = ctypes.c_double
+    lib.tdgp_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.tdgp_mfma_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = lib.tdgp_operand_elems()
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator().manual_seed(4)
+    out = {"kernel": "per-wave 16x16x32 bf16 MFMA stream of the 256x256 kernel (8x4 accumulator tiles, "
+                     "2 K sub-steps per K tile), operands in registers, 8 waves per CU",
+           "workgroups": blocks}
+    for name, ops in (("random_normal", torch.randn(n, generator=gen).to(torch.bfloat16)),
+                      ("zeros", torch.zeros(n, dtype=torch.bfloat16))):
+        ops = ops.to(dev)
+
+        def run(iters):
+            rc = lib.tdgp_mfma_stream(ops.data_ptr(), iters, blocks, sink.data_ptr(), clocks.data_ptr(),
+                                      ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError("tdgp_mfma_stream returned %d" % rc)
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        iters = 2000
+        t_end = time.perf_counter() + 0.2           # load the engine long enough for its clock to settle
+        while time.perf_counter() < t_end:
+            e0.record(stream)
+            run(iters)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            iters = max(iters, int(iters * 0.05 / max(e0.elapsed_time(e1) * 1e-3, 1e-6)))
+        iters = max(1, int(iters * seconds / 0.05))
+        e0.record(stream)
+        run(iters)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        ck = clocks.view(blocks, 2).double().cpu()
+        ghz = float((ck[:, 0] / ck[:, 1]).mean()) * 0.1
+        out[name] = {"tflops": round(lib.tdgp_flops(iters, blocks) / (ms * 1e-3) / 1e12, 1),
+                     "clock_ghz": round(ghz, 3), "ms": round(ms, 3)}
+    return out
+
+
 def gpu_state_under_load(tdg, torch, w, kernel_ms, seconds=1.5):
     """amd-smi sampled while the GPU runs back-to-back launches of the
     workload (about `seconds` of them, queued before the sample is taken)."""
@@ -263,6 +322,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true", help="skip the amd-smi clock/temperature sample")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-stream ceiling probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -361,6 +421,11 @@ def main():
                          "scales": ("E8M0 per 32-element K block" if wf.block_scales else "none") +
                                    (" + fp32 per row" if wf.row_scales else "")})
         line["also"] = also
+    if not args.no_ceiling and w.in_dtype in ("f16", "bf16"):
+        ceil = mfma_ceiling(torch)
+        ceil["headline_frac_of_random_ceiling"] = round(achieved / ceil["random_normal"]["tflops"], 4)
+        ceil["random_ceiling_frac_of_peak"] = round(ceil["random_normal"]["tflops"] / peak, 4)
+        line["mfma_ceiling"] = ceil
     if not args.no_gpu_state:
         line["gpu_state"] = gpu_state_under_load(tdg, torch, w, kernel_ms)
     if not args.no_cpu_baseline:

@@ -1,0 +1,64 @@
+/*
+ * tdg_probe.h -- measurement probe that sits beside the GEMM library
+ * (libtdg_probe.so).  It is not a product call: it measures the ceiling that
+ * the dense-contraction kernels of libtdg.so run against.
+ *
+ * What it measures.  The bf16 GEMM kernel's inner K loop is, per wave, a fixed
+ * stream of v_mfma_f32_16x16x32_bf16 instructions: a 128 x 64 wave tile held
+ * as 8 x 4 accumulator tiles of 16 x 16 fp32, updated twice per 64-wide K tile
+ * (two K sub-steps of 32), each sub-step taking 8 A fragments and 4 B
+ * fragments.  The probe runs that same instruction stream with the operand
+ * fragments held in registers -- no global loads, no LDS, no barriers -- so
+ * its rate is the most the MFMA pipes sustain on those operand values at the
+ * clock the chip holds under that load.  The engine clock of this part is
+ * limited by board power, and the power an MFMA draws depends on its operand
+ * bits: random operands clock lower than zeros.  Feeding the probe the same
+ * distribution as a GEMM's inputs gives the practical ceiling for that GEMM.
+ *
+ * The dense-contraction definition the kernels implement is in tdg.h; the
+ * tile and fragment shapes above are the kernel's own (see
+ * tiled_dense_gemm_03_amd/csrc/gemm_m16.hpp), chosen for gfx950.
+ */
+#ifndef TDG_PROBE_H
+#define TDG_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of bf16 elements the operand array of tdgp_mfma_stream must hold:
+ * 24 fragments (2 sub-steps x (8 A + 4 B)) x 512 lanes x 8 elements. */
+size_t tdgp_operand_elems(void);
+
+/* Enqueue the MFMA stream on `stream` (a hipStream_t; NULL = null stream).
+ *   operands  device, bf16 bit patterns, tdgp_operand_elems() elements:
+ *             fragment f of lane l (l = thread index in a 512-thread
+ *             workgroup) is elements [(f * 512 + l) * 8, +8); fragments 0..7
+ *             are sub-step 0's A, 8..11 its B, 12..19 sub-step 1's A, 20..23
+ *             its B.  Every workgroup reads the same array.
+ *   iters     K tiles to run (64 MFMAs per wave each); 1 <= iters <= 2^31.
+ *   blocks    workgroups of 512 threads (8 waves); 1 <= blocks <= 65536.
+ *             One per CU (256) keeps every MFMA pipe of the chip busy.
+ *   sink      device fp32[blocks * 512]: each lane writes the sum of its 128
+ *             accumulator values (so the stream cannot be optimised away; with
+ *             every operand equal to 1.0 each lane writes 8192 * iters).
+ *   clocks    device uint64[blocks * 2], or NULL: per workgroup, the shader
+ *             clock ticks and the 100 MHz constant-clock ticks that its first
+ *             wave spent in the stream; their ratio x 100 MHz is the mean
+ *             engine clock.
+ * Returns 0 on success, 1 for an argument out of range or a NULL pointer
+ * (nothing enqueued), 3 when the launch was rejected.  The caller owns every
+ * buffer; nothing is allocated and nothing synchronises. */
+int tdgp_mfma_stream(const void *operands, int64_t iters, int blocks, float *sink, uint64_t *clocks, void *stream);
+
+/* FLOPs one call performs: 2 * 16 * 16 * 32 * 64 * 8 * blocks * iters. */
+double tdgp_flops(int64_t iters, int blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDG_PROBE_H */

@@ -237,3 +237,35 @@ def test_f8_invalid_arguments_rejected_before_launch(tdg, kw, status, needle):
 def test_f8_degenerate_sizes_succeed_without_a_device(tdg):
     assert _f8_call(tdg, M=0) == tdg.TDG_SUCCESS
     assert _f8_call(tdg, N=0, A=None, B=None, C=None) == tdg.TDG_SUCCESS
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "tdg_probe.h")
+PROBE_LIB = os.path.join(ROOT, "tiled_dense_gemm_03_amd", "libtdg_probe.so")
+
+
+def test_probe_library_exports_its_header(tdg):
+    """The MFMA ceiling probe beside the library: every function its header
+    declares is exported, and bad arguments are refused before any launch."""
+    import ctypes
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tdgp_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["tdgp_flops", "tdgp_mfma_stream", "tdgp_operand_elems"]
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    assert set(names) <= exported
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tdgp_operand_elems.restype = ctypes.c_size_t
+    lib.tdgp_flops.restype = ctypes.c_double
+    lib.tdgp_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.tdgp_mfma_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tdgp_operand_elems() == 24 * 512 * 8
+    # 64 MFMAs of 16x16x32 per wave per K tile, 8 waves per workgroup
+    assert lib.tdgp_flops(3, 5) == 2.0 * 16 * 16 * 32 * 64 * 8 * 5 * 3
+    fake = 1 << 20                           # never dereferenced: each call below fails its checks first
+    assert lib.tdgp_mfma_stream(None, 1, 1, fake, None, None) == 1
+    assert lib.tdgp_mfma_stream(fake, 1, 1, None, None, None) == 1
+    assert lib.tdgp_mfma_stream(fake + 8, 1, 1, fake, None, None) == 1     # operands not 16-byte aligned
+    assert lib.tdgp_mfma_stream(fake, 0, 1, fake, None, None) == 1
+    assert lib.tdgp_mfma_stream(fake, 1, 0, fake, None, None) == 1
+    assert lib.tdgp_mfma_stream(fake, 1, 65537, fake, None, None) == 1

@@ -1,0 +1,84 @@
+// MFMA ceiling probe (libtdg_probe.so): the per-wave 16x16x32 bf16 MFMA stream
+// of the 256 x 256 GEMM kernel with the operands held in registers, timed to
+// give the rate the matrix cores sustain on a given operand distribution at
+// the clock the chip holds under that load.  Interface and buffer layout are
+// described in include/tdg_probe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tdg_probe.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLanes = 512;       // threads per workgroup: 8 waves, 2 per SIMD
+constexpr int kFragments = 24;    // 2 K sub-steps x (8 A + 4 B)
+constexpr int kWaveRows = 8;      // 16-row accumulator tiles per wave (128 rows)
+constexpr int kWaveCols = 4;      // 16-column accumulator tiles per wave (64 columns)
+
+__global__ __launch_bounds__(kLanes) void mfma_stream_kernel(const bf16x8 *__restrict__ ops, int64_t iters,
+                                                             float *__restrict__ sink,
+                                                             uint64_t *__restrict__ clocks) {
+    const int t = threadIdx.x;
+    bf16x8 a[2][kWaveRows], b[2][kWaveCols];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < kWaveRows; ++i) a[s][i] = ops[(s * 12 + i) * kLanes + t];
+#pragma unroll
+        for (int j = 0; j < kWaveCols; ++j) b[s][j] = ops[(s * 12 + kWaveRows + j) * kLanes + t];
+    }
+    f32x4 acc[kWaveRows][kWaveCols];
+#pragma unroll
+    for (int i = 0; i < kWaveRows; ++i)
+#pragma unroll
+        for (int j = 0; j < kWaveCols; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < kWaveRows; ++i)
+#pragma unroll
+                for (int j = 0; j < kWaveCols; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][i], b[s][j], acc[i][j], 0, 0, 0);
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaveRows; ++i)
+#pragma unroll
+        for (int j = 0; j < kWaveCols; ++j) sum += (acc[i][j][0] + acc[i][j][1]) + (acc[i][j][2] + acc[i][j][3]);
+    sink[(int64_t)blockIdx.x * kLanes + t] = sum;
+    if (clocks != nullptr && t == 0) {
+        clocks[2 * (int64_t)blockIdx.x] = c1 - c0;
+        clocks[2 * (int64_t)blockIdx.x + 1] = r1 - r0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tdgp_operand_elems(void) { return (size_t)kFragments * kLanes * 8; }
+
+double tdgp_flops(int64_t iters, int blocks) {
+    return 2.0 * 16 * 16 * 32 * (2 * kWaveRows * kWaveCols) * (kLanes / 64) * (double)blocks * (double)iters;
+}
+
+int tdgp_mfma_stream(const void *operands, int64_t iters, int blocks, float *sink, uint64_t *clocks, void *stream) {
+    if (operands == nullptr || sink == nullptr) return 1;
+    if (((uintptr_t)operands & 15) != 0) return 1;
+    if (iters < 1 || iters > ((int64_t)1 << 31) || blocks < 1 || blocks > 65536) return 1;
+    hipLaunchKernelGGL(mfma_stream_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, (hipStream_t)stream,
+                       static_cast<const bf16x8 *>(operands), iters, sink, clocks);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+}  // extern "C"
