@@ -118,12 +118,16 @@ def test_config_selection(tdg):
         ldb = ldb or (K if transb else N)
         return tdg.tdg_config_name(tdg.tdg_select_config(transb, M, N, K, a, lda, b, ldb, P, N, batch, 0, c_type))
     assert sel(0, 8192, 8192, 8192) == "256x256x64_s2_w2x4_m16"
-    assert sel(1, 8192, 8192, 8192) == "256x256x64_s2_w2x4_m16p"
+    assert sel(1, 8192, 8192, 8192) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 8192, 8192, 8192, c_type=2) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 4096, 4096, 4096) == "256x256x64_s2_w2x4_m16"
     assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16"
+    # the persistent kernel: several rounds of 256 x 256 tiles and K <= 512
     assert sel(1, 2048, 2048, 128, batch=32) == "256x256x64_s2_w2x4_m16p"
-    assert sel(1, 2048, 2048, 128, batch=32, c_type=2) == "256x256x64_s2_w2x4_m16"
+    assert sel(1, 2048, 2048, 128, batch=32, c_type=2) == "256x256x64_s2_w2x4_m16p"
+    assert sel(0, 4096, 4096, 512, batch=4) == "256x256x64_s2_w2x4_m16p"
+    assert sel(0, 4096, 4096, 520, batch=4) == "256x256x64_s2_w2x4_m16"
+    assert sel(1, 4096, 4096, 256) == "256x256x64_s2_w2x4_m16"          # a single round
     assert sel(0, 1024, 1024, 1024) == "128x128x64_s4_w2x4_m16"
     assert sel(0, 65, 97, 130).endswith("_pred")            # K not a multiple of 8
     assert not sel(1, 64, 97, 128).endswith("_pred")        # TN: N may be ragged

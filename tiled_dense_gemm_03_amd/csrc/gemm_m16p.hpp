@@ -13,8 +13,9 @@
 //    and no tile after the first waits for the full load latency.
 //  * The epilogue runs between two K iterations, while the stages already
 //    hold the next tile's operands, so it goes through a small staging area
-//    of its own (per wave, 16 rows of 16-bit values or 8 rows of fp32); the
-//    stores of one tile drain while the next tile computes.
+//    of its own (per wave, 16 rows of 16-bit values; for fp32, 16 rows of
+//    each wave row as whole tile rows); the stores of one tile drain while
+//    the next tile computes.
 //
 // The NineToothed primer's decomposition (s4: one program per output tile,
 // K as a loop in the program) is unchanged: a workgroup runs several
@@ -46,13 +47,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
     constexpr int NVB = TRANSB ? 1 : 16 / ((NW * RPB) % 16 == 0 ? 16 : ((NW * RPB) % 8 == 0 ? 8 : ((NW * RPB) % 4 == 0 ? 4 : ((NW * RPB) % 2 == 0 ? 2 : 1))));
     constexpr int NVA = !TRANSA ? 1 : 16 / ((NW * RPA) % 16 == 0 ? 16 : ((NW * RPA) % 8 == 0 ? 8 : ((NW * RPA) % 4 == 0 ? 4 : ((NW * RPA) % 2 == 0 ? 2 : 1))));
 
-    // A per-wave staging area outside the stages (which hold the next
-    // tile's operands when the epilogue runs): one 16-row block of the
-    // wave's sub-tile in 16-bit values, or half a block in fp32.
+    // A staging area outside the stages (which hold the next tile's
+    // operands when the epilogue runs).  16-bit output: per wave, one 16-row
+    // block of its sub-tile.  fp32 output: one 16-row block of every wave
+    // row, held as whole tile rows (WM x 16 rows of BN * 4 bytes, 16-byte
+    // chunks XOR-swizzled by the row so neither the writes nor the reads
+    // conflict; no padding, so 2 x 16 rows of 1 KiB fill what two 64 KiB
+    // stages leave of the LDS).
     constexpr int ES = (CT == OUT_F32) ? 4 : 2;
-    constexpr int SROW = WTN * ES + 16;                      // staged row, padded by 16 bytes
-    constexpr int SR = (CT == OUT_F32) ? 8 : 16;             // rows staged at a time
-    constexpr int STG = NW * SR * SROW / 16;
+    constexpr int SROW = WTN * ES + 16;                      // staged row (16-bit), padded by 16 bytes
+    constexpr int SR = 16;                                   // rows staged at a time (16-bit)
+    constexpr int RB = BN * 4;                               // bytes of a tile row (fp32)
+    constexpr int CPR32 = RB / 16;                           // 16-byte chunks of a tile row (fp32)
+    static_assert(CT != OUT_F32 || (CPR32 >= 16 && (CPR32 & (CPR32 - 1)) == 0 && 64 % CPR32 == 0),
+                  "fp32 tile rows: a power of two of 16..64 chunks");
+    constexpr int STG = (CT == OUT_F32) ? WM * 16 * CPR32 : NW * SR * SROW / 16;
     static_assert((STAGE * STAGES + STG) * 16 <= 160 * 1024, "LDS budget");
     __shared__ u32x4 smem[STAGES * STAGE + STG];
 
@@ -243,6 +252,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
         const char *Cbase = (const char *)p.C + ((int64_t)batch * p.sC + (int64_t)(m0 + wave_m * WTM) * p.ldc +
                                                  n0 + wave_n * WTN) * ES;
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase);
+        const __amdgpu_buffer_rsrc_t rc_tile =
+            make_rsrc((const char *)p.C + ((int64_t)batch * p.sC + (int64_t)m0 * p.ldc + n0) * ES);
         const bool vec_store = (n0 + BN <= N) && c_aligned;
         const int cols_left = N - n0 - wave_n * WTN - 4 * fg;      // valid columns from the lane's first one
 #pragma unroll
@@ -298,33 +309,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                 if (CT != OUT_F32 || !vec_store) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
             if constexpr (CT == OUT_F32) {
-                // rows 8 h .. 8 h + 7 of the block: written by the lanes that
-                // hold them, read back as 4 rows x 16 pieces per instruction
-                constexpr int CPR = WTN * 4 / 16, RPI = 64 / CPR, NT = SR / RPI;
-                static_assert(CPR * RPI == 64 && SR % RPI == 0, "row pieces must tile a wave");
+                // block i of every wave row at once (vec_store is uniform over
+                // the workgroup): staged row R = wave_m * 16 + fr holds tile row
+                // wave_m * WTM + 16 i + fr; each wave then stores whole tile
+                // rows, RPI rows of CPR32 chunks per instruction.
+                constexpr int RPI = 64 / CPR32, PRW = WM * 16, NT = PRW / (NW * RPI);
+                static_assert(NT * NW * RPI == PRW, "staged rows spread evenly over the waves");
                 if (vec_store) {
+                    char *const stg = reinterpret_cast<char *>(smem + STAGES * STAGE);
+                    if (i > 0) __syncthreads();                  // block i - 1 has been read back
+                    const int R = wave_m * 16 + fr;
 #pragma unroll
-                    for (int h = 0; h < 16 / SR; ++h) {
-                        if (fr / SR == h) {
-#pragma unroll
-                            for (int j = 0; j < RN; ++j)
-                                *reinterpret_cast<f32x4 *>(stage_w + (16 * j + 4 * fg) * 4) = acc[i][j];
-                        }
-                        u32x4 w[NT];
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            const int row = t * RPI + lane / CPR, piece = lane % CPR;
-                            w[t] = *reinterpret_cast<const u32x4 *>(stage_r + row * SROW + piece * 16);
-                        }
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            const int row = h * SR + t * RPI + lane / CPR, piece = lane % CPR;
-                            const uint32_t off =
-                                row < rows_left ? (uint32_t)(row * p.ldc + piece * 4) * ES : OOB_OFFSET;
-                            __builtin_amdgcn_raw_buffer_store_b128(w[t], rc, off, so_row, STORE_NT);
-                        }
-                        store_data_read_all(w);
+                    for (int j = 0; j < RN; ++j) {
+                        const int c = (wave_n * WTN + 16 * j + 4 * fg) / 4;
+                        *reinterpret_cast<f32x4 *>(stg + R * RB + ((c ^ (R & 15)) * 16)) = acc[i][j];
                     }
+                    __syncthreads();
+                    u32x4 w[NT];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int Rr = (wave * NT + t) * RPI + lane / CPR32, c = lane % CPR32;
+                        w[t] = *reinterpret_cast<const u32x4 *>(stg + Rr * RB + ((c ^ (Rr & 15)) * 16));
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int Rr = (wave * NT + t) * RPI + lane / CPR32, c = lane % CPR32;
+                        const int row = (Rr / 16) * WTM + 16 * i + Rr % 16;     // row of the tile
+                        const uint32_t off =
+                            m0 + row < M ? (uint32_t)(row * p.ldc + c * 4) * ES : OOB_OFFSET;
+                        __builtin_amdgcn_raw_buffer_store_b128(w[t], rc_tile, off, 0, STORE_NT);
+                    }
+                    store_data_read_all(w);
 #pragma unroll
                     for (int j = 0; j < RN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }

@@ -186,24 +186,27 @@ bool split_pays(const SplitPlan &pl, int64_t cus) {
 
 // Tile-configuration choice (measured on MI355X), with `cus` the device's
 // compute units: 256 x 256 tiles on the 16 x 16 x 32 MFMA kernel when the
-// problem has at least one such tile per CU (its persistent form for TN
-// products of several rounds with 16-bit output); 128 x 128 tiles on the same
+// problem has at least one such tile per CU (its persistent form for
+// problems of several rounds with a short K); 128 x 128 tiles on the same
 // kernel (8 waves, 4 stages) for smaller problems; the 32 x 32 x 16 direct
 // load kernel or the register-staged kernel when the 16 x 16 x 32 kernel
 // cannot address the operands; the predicated kernel for misaligned
 // operands.
 // An A stored K x M (transa) has only the 16 x 16 x 32 kernel: -1 when that
 // kernel cannot serve the operands.
-int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t batch, int64_t lda, int64_t ldb,
-           int64_t ldc, int c_type, int64_t cus) {
+int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t K, int64_t batch, int64_t lda,
+           int64_t ldb, int64_t ldc, int c_type, int64_t cus) {
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
-        // several rounds of K-contiguous operands with 16-bit output: the
-        // persistent form (measured +5% on 8192^3 TN; no gain on NN, where
-        // the NN-B loads are less latency-bound, nor in a single round)
+        // several rounds with K <= 512 (at most 8 K tiles per output tile):
+        // the persistent form, whose next tile's loads and MFMAs overlap the
+        // current tile's stores (4 x 4096^2 x K, both layouts, 16-bit and
+        // fp32 output: 14-24% faster at K = 128..256, 0.6-15% at 512, even at
+        // 1024, 1-12% slower from 2048 on, where the one-tile kernel's wave
+        // priority and simpler loop win); not in a single round
         const int pid = config_by_name("256x256x64_s2_w2x4_m16p");
-        if (tiles256 >= 2 * cus && transb && !transa && c_type != TDG_F32 &&
+        if (tiles256 >= 2 * cus && K > 0 && K <= 512 && !transa &&
             config_ok(kConfigs[pid], transa, transb, vec, lda, ldb, ldc, c_type))
             return pid;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
@@ -443,7 +446,7 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
             tuned = true;
         }
     }
-    if (automatic && !tuned) config = choose(transa, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    if (automatic && !tuned) config = choose(transa, transb, vec, M, N, K, batch, lda, ldb, ldc, c_type, cus);
     if (config < 0)
         return fail(TDG_NOT_SUPPORTED,
                     "layout transa=%d transb=%d transc=%d runs on the vectorised kernel only: 16-byte aligned A and B, "
@@ -659,7 +662,7 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
     int cus = num_cus;
     if (cus <= 0 && tdg::check_device(&cus) != TDG_SUCCESS) return 0;
     // the configuration the library picks for vectorisable operands
-    const int id = tdg::choose(0, transb, true, M, N, batch, K, transb ? K : N, N, TDG_F32, cus);
+    const int id = tdg::choose(0, transb, true, M, N, K, batch, K, transb ? K : N, N, TDG_F32, cus);
     if (id < 0) return 0;
     const tdg::Config &cf = tdg::kConfigs[id];
     if (cf.kind != 2) return 0;
@@ -769,7 +772,7 @@ int tdg_select_config(int transb, int64_t M, int64_t N, int64_t K, const void *A
         const int t = tdg::tuned_config(tdg::TuneKey{dev, 0, transb, 0, ab_type, c_type, vec ? 1 : 0, M, N, K, batch});
         if (t >= 0) return t;
     }
-    return tdg::choose(0, transb, vec, M, N, batch, lda, ldb, ldc, c_type, cus);
+    return tdg::choose(0, transb, vec, M, N, K, batch, lda, ldb, ldc, c_type, cus);
 }
 
 const char *tdg_status_string(tdg_status status) {
