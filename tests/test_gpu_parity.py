@@ -478,6 +478,23 @@ def test_autotune_transposed_operands(tdg):
 # Persistent form of the 16x16x32 kernel: workgroups walking several tiles
 # ---------------------------------------------------------------------------
 
+# The library's own choice of the persistent kernel: two or more rounds of
+# 256 x 256 tiles with K <= 512, in both layouts and with 16-bit and fp32
+# output (the automatic path, not a forced configuration).
+@pytest.mark.parametrize("layout,M,N,K,batch,in_dtype,out_dtype", [("nn", 4096, 4096, 320, 2, "bf16", "bf16"),
+                                                                   ("tn", 6100, 5400, 192, 0, "f16", "f32"),
+                                                                   ("nn", 2048, 2048, 512, 8, "f16", "f32")])
+def test_automatic_persistent_choice_exact(tdg, layout, M, N, K, batch, in_dtype, out_dtype):
+    announce("auto persistent", layout, M, N, K, batch, in_dtype, out_dtype)
+    a, b = make_inputs(M, N, K, layout, in_dtype, "ints", seed=M + K + batch, batch=batch)
+    ad, bd = a.cuda(), b.cuda()
+    assert tdg.config_names()[tdg.select_config(ad, bd, layout, OUT_TORCH[out_dtype])].endswith("_m16p")
+    c = gpu_gemm(tdg, a, b, layout, out_dtype)
+    rows = sample_rows(M)
+    ref = ref_gemm(a, b, in_dtype, layout, rows=rows)
+    check_exact(c[:, rows] if batch else c[rows], ref, out_dtype, "auto persistent %s %dx%dx%d b%d" % (layout, M, N, K, batch))
+
+
 # (layout, M, N, K, batch): more 256 x 256 tiles than CUs, so workgroups take
 # two or more tiles; ragged M, N and K tails; K = 64 (one K tile: the loads
 # run ahead across several tiles); a batch whose tiles switch problems.
