@@ -34,7 +34,7 @@ extern "C" {
 size_t tdgp_operand_elems(void);
 
 /* Enqueue the MFMA stream on `stream` (a hipStream_t; NULL = null stream).
- *   operands  device, bf16 bit patterns, tdgp_operand_elems() elements:
+ *   operands  device, 16-byte aligned, bf16 bit patterns, tdgp_operand_elems() elements:
  *             fragment f of lane l (l = thread index in a 512-thread
  *             workgroup) is elements [(f * 512 + l) * 8, +8); fragments 0..7
  *             are sub-step 0's A, 8..11 its B, 12..19 sub-step 1's A, 20..23
@@ -49,8 +49,8 @@ size_t tdgp_operand_elems(void);
  *             clock ticks and the 100 MHz constant-clock ticks that its first
  *             wave spent in the stream; their ratio x 100 MHz is the mean
  *             engine clock.
- * Returns 0 on success, 1 for an argument out of range or a NULL pointer
- * (nothing enqueued), 3 when the launch was rejected.  The caller owns every
+ * Returns 0 on success, 1 for an argument out of range, a NULL pointer or
+ * misaligned operands (nothing enqueued), 3 when the launch was rejected.  The caller owns every
  * buffer; nothing is allocated and nothing synchronises. */
 int tdgp_mfma_stream(const void *operands, int64_t iters, int blocks, float *sink, uint64_t *clocks, void *stream);
 
