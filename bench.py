@@ -17,7 +17,9 @@ the launches run back to back, so the span is their durations plus the
 small gaps between them).  The other workloads are timed the same way over
 at least 50 ms of launches, five times, and report the medians; the
 HBM-bound batched product is also timed with the caches emptied before
-each launch.  "mfma_ceiling" is the rate of the bf16 kernel's MFMA stream
+each launch.  "small" gives the per-call cost of the two small workloads
+(host time of a C-ABI call and of the Python wrapper, kernel time, wall
+time per call).  "mfma_ceiling" is the rate of the bf16 kernel's MFMA stream
 with its operands in registers (libtdg_probe.so), on the headline's operand
 distribution and on zeros: the engine clock is power-limited and depends on
 the operand bits, so this, not the published peak, is what the MFMA-bound
@@ -120,6 +122,51 @@ def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_t
     wall_ms, kernel_ms = timed_runs(torch, call, stream, steps, repeats, min_total_s)
     cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
     return wall_ms, kernel_ms, tdg.tdg_config_name(cfg)
+
+
+def time_small(tdg, torch, w, calls=3000):
+    """Per-call cost of a small workload, where the fixed cost of a call
+    dominates: the host time of one C-ABI call (argument checks, tile choice,
+    enqueue; the GPU runs behind), the same through the Python wrapper, the
+    kernel's duration from an event pair around back-to-back launches, and
+    the wall time per call of the whole run (host and GPU)."""
+    from workloads import TORCH_DTYPE, workload_inputs
+    a, b = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    a, b = a.to(dev), b.to(dev)
+    c = torch.empty((w.M, w.N), dtype=TORCH_DTYPE[w.out_dtype], device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = {"f16": 0, "bf16": 1, "f32": 2}
+    fn = tdg._binding.lib.tdg_gemm_tn if w.layout == "tn" else tdg._binding.lib.tdg_gemm_nn
+    args = (w.M, w.N, w.K, a.data_ptr(), w.K, b.data_ptr(), w.K if w.layout == "tn" else w.N, c.data_ptr(), w.N,
+            code[w.in_dtype], code[w.out_dtype], stream.cuda_stream)
+    if fn(*args) != 0:
+        raise RuntimeError("tdg_gemm_%s failed on %s" % (w.layout, w.name))
+
+    def craw():
+        fn(*args)
+
+    def cpy():
+        tdg.gemm(a, b, layout=w.layout, out=c)
+    out = {"workload": w.name, "calls": calls}
+    for name, call in (("c_abi", craw), ("python", cpy)):
+        for _ in range(300):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(calls):
+            call()
+        t1 = time.perf_counter()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        out[name] = {"host_us_per_call": round((t1 - t0) / calls * 1e6, 2),
+                     "wall_us_per_call": round((t2 - t0) / calls * 1e6, 2),
+                     "gpu_us_per_call": round(e0.elapsed_time(e1) / calls * 1e3, 2)}
+    out["tflops_c_abi"] = round(w.flops / (out["c_abi"]["wall_us_per_call"] * 1e-6) / 1e12, 2)
+    return out
 
 
 def time_flushed(tdg, torch, w, reps=20):
@@ -420,6 +467,8 @@ def main():
                          "dtype": wf.a_fmt, "out_dtype": wf.out_dtype,
                          "scales": ("E8M0 per 32-element K block" if wf.block_scales else "none") +
                                    (" + fp32 per row" if wf.row_scales else "")})
+        # the two small workloads: the fixed cost of a call
+        line["small"] = [time_small(tdg, torch, WORKLOADS[n]) for n in ("worked_128x256x192", "tn_exact_1024")]
         line["also"] = also
     if not args.no_ceiling and w.in_dtype in ("f16", "bf16"):
         ceil = mfma_ceiling(torch)

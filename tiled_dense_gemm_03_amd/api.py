@@ -76,6 +76,9 @@ def select_config(a, b, layout="nn", out_dtype=None):
 # the same time never share one; zero-filled once by torch, kept zero-filled by
 # the library.  Replaced by a larger one when a call needs more.
 _workspaces = {}
+# Workspace bytes the library asks for, per problem (the answer depends only
+# on the sizes and the device's compute-unit count).
+_ws_need = {}
 
 
 def _workspace(device, stream, nbytes):
@@ -132,24 +135,38 @@ def gemm(a, b, layout="nn", out_dtype=None, out=None, config=-1, split_k=True):
     (a workspace per device and stream, allocated by torch once).
     """
     ta, tb, tc, M, N, K, lda, sA, ldb, sB, ldc, sC, batch, odt, out = _marshal(a, b, layout, out_dtype, out)
-    stream = torch.cuda.current_stream(a.device).cuda_stream
-    with torch.cuda.device(a.device):
-        if config == -1:
-            need = _b.tdg_gemm_workspace_size(tb, M, N, K, batch, 0) if split_k else 0
-            ws = _workspace(a.device, stream, need) if need else None
-            _check(_b.tdg_gemm(ta, tb, tc, M, N, K,
-                               a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
-                               out.data_ptr(), ldc, sC, batch,
-                               _AB[a.dtype], _CT[odt],
-                               ws.data_ptr() if ws is not None else None,
-                               ws.numel() if ws is not None else 0, stream))
-        else:
-            if ta or tc:
-                raise ValueError("a forced configuration takes row-major a and out")
-            _check(_b.tdg_gemm_ex(tb, M, N, K,
-                                  a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB,
-                                  out.data_ptr(), ldc, sC, batch,
-                                  _AB[a.dtype], _CT[odt], int(config), stream))
+    dev = a.device
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if config == -1:
+        ws = None
+        if split_k:
+            key = (tb, M, N, K, batch, dev.index)
+            need = _ws_need.get(key)
+            if need is None:
+                with torch.cuda.device(dev):
+                    need = _b.tdg_gemm_workspace_size(tb, M, N, K, batch, 0)
+                if len(_ws_need) >= 4096:
+                    _ws_need.clear()
+                _ws_need[key] = need
+            if need:
+                ws = _workspace(dev, stream, need)
+        args = (ta, tb, tc, M, N, K, a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB, out.data_ptr(), ldc, sC, batch,
+                _AB[a.dtype], _CT[odt], ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0, stream)
+        call = _b.lib.tdg_gemm
+    else:
+        if ta or tc:
+            raise ValueError("a forced configuration takes row-major a and out")
+        args = (tb, M, N, K, a.data_ptr(), lda, sA, b.data_ptr(), ldb, sB, out.data_ptr(), ldc, sC, batch,
+                _AB[a.dtype], _CT[odt], int(config), stream)
+        call = _b.lib.tdg_gemm_ex
+    # the library launches on the current device: make it a's (the common
+    # case needs no switch)
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        _check(call(*args))
+    else:
+        with torch.cuda.device(dev):
+            _check(call(*args))
     return out
 
 
