@@ -276,37 +276,35 @@ def amd_smi_state():
 
 
 def mfma_ceiling(torch, seconds=0.25):
-    """Rate of the bf16 GEMM kernel's per-wave MFMA stream with its operands
-    held in registers (libtdg_probe.so, no memory traffic), one 8-wave
-    workgroup per CU, on N(0, 1) bf16 operands (the headline's inputs) and on
-    zeros: the practical ceiling of the MFMA-bound products at the clock the
-    board's power limit allows for those operand bits."""
+    """Rates of the kernels' per-wave MFMA streams with their operands held
+    in registers (libtdg_probe.so, no memory traffic), one 8-wave workgroup
+    per CU: the bf16 stream on N(0, 1) bf16 operands (the headline's inputs)
+    and on zeros, the 8-bit stream on N(0, 1) E4M3 operands (the 8-bit legs'
+    inputs) and on zeros.  The practical ceiling of the MFMA-bound products
+    at the clock the board's power limit allows for those operand bits."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "tiled_dense_gemm_03_amd", "libtdg_probe.so"))
-    lib.tdgp_operand_elems.restype = ctypes.c_size_t
-    lib.tdgp_flops.restype = ctypes.c_double
-    lib.tdgp_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
-    lib.tdgp_mfma_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_void_p]
+    argt = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for f in ("tdgp_operand_elems", "tdgp_operand_bytes_f8"):
+        getattr(lib, f).restype = ctypes.c_size_t
+    for f in ("tdgp_flops", "tdgp_flops_f8"):
+        getattr(lib, f).restype = ctypes.c_double
+        getattr(lib, f).argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.tdgp_mfma_stream.argtypes = argt
+    lib.tdgp_mfma_stream_f8.argtypes = argt
     dev = torch.device("cuda")
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
-    n = lib.tdgp_operand_elems()
     sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
     clocks = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
     gen = torch.Generator().manual_seed(4)
-    out = {"kernel": "per-wave 16x16x32 bf16 MFMA stream of the 256x256 kernel (8x4 accumulator tiles, "
-                     "2 K sub-steps per K tile), operands in registers, 8 waves per CU",
-           "workgroups": blocks}
-    for name, ops in (("random_normal", torch.randn(n, generator=gen).to(torch.bfloat16)),
-                      ("zeros", torch.zeros(n, dtype=torch.bfloat16))):
-        ops = ops.to(dev)
 
+    def measure(launch, flops, ops):
         def run(iters):
-            rc = lib.tdgp_mfma_stream(ops.data_ptr(), iters, blocks, sink.data_ptr(), clocks.data_ptr(),
-                                      ctypes.c_void_p(stream.cuda_stream))
+            rc = launch(ops.data_ptr(), iters, blocks, sink.data_ptr(), clocks.data_ptr(),
+                        ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
-                raise RuntimeError("tdgp_mfma_stream returned %d" % rc)
+                raise RuntimeError("MFMA probe returned %d" % rc)
 
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         iters = 2000
@@ -325,8 +323,23 @@ def mfma_ceiling(torch, seconds=0.25):
         ms = e0.elapsed_time(e1)
         ck = clocks.view(blocks, 2).double().cpu()
         ghz = float((ck[:, 0] / ck[:, 1]).mean()) * 0.1
-        out[name] = {"tflops": round(lib.tdgp_flops(iters, blocks) / (ms * 1e-3) / 1e12, 1),
-                     "clock_ghz": round(ghz, 3), "ms": round(ms, 3)}
+        return {"tflops": round(flops(iters, blocks) / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(ghz, 3),
+                "ms": round(ms, 3)}
+
+    n = lib.tdgp_operand_elems()
+    out = {"kernel": "per-wave 16x16x32 bf16 MFMA stream of the 256x256 kernel (8x4 accumulator tiles, "
+                     "2 K sub-steps per K tile), operands in registers, 8 waves per CU",
+           "workgroups": blocks}
+    for name, ops in (("random_normal", torch.randn(n, generator=gen).to(torch.bfloat16)),
+                      ("zeros", torch.zeros(n, dtype=torch.bfloat16))):
+        out[name] = measure(lib.tdgp_mfma_stream, lib.tdgp_flops, ops.to(dev))
+    n8 = lib.tdgp_operand_bytes_f8()
+    f8 = {"kernel": "per-wave scaled 32x32x64 E4M3 MFMA stream of the 8-bit 256x256 kernel (4x2 accumulator "
+                    "tiles, 2 K sub-steps per K tile, unit scales), operands in registers, 8 waves per CU"}
+    for name, ops in (("random_normal", torch.randn(n8, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)),
+                      ("zeros", torch.zeros(n8, dtype=torch.uint8))):
+        f8[name] = measure(lib.tdgp_mfma_stream_f8, lib.tdgp_flops_f8, ops.to(dev))
+    out["e4m3"] = f8
     return out
 
 
@@ -474,6 +487,11 @@ def main():
         ceil = mfma_ceiling(torch)
         ceil["headline_frac_of_random_ceiling"] = round(achieved / ceil["random_normal"]["tflops"], 4)
         ceil["random_ceiling_frac_of_peak"] = round(ceil["random_normal"]["tflops"] / peak, 4)
+        c8 = ceil["e4m3"]["random_normal"]["tflops"]
+        ceil["e4m3"]["random_ceiling_frac_of_peak"] = round(c8 / PEAK_TFLOPS["e4m3"], 4)
+        for entry in line.get("also", []):
+            if entry.get("dtype") == "e4m3":
+                entry["frac_of_random_ceiling"] = round(entry["kernel_tflops"] / c8, 4)
         line["mfma_ceiling"] = ceil
     if not args.no_gpu_state:
         line["gpu_state"] = gpu_state_under_load(tdg, torch, w, kernel_ms)

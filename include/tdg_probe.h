@@ -57,6 +57,23 @@ int tdgp_mfma_stream(const void *operands, int64_t iters, int blocks, float *sin
 /* FLOPs one call performs: 2 * 16 * 16 * 32 * 64 * 8 * blocks * iters. */
 double tdgp_flops(int64_t iters, int blocks);
 
+/* The same for the 8-bit kernel's stream: per wave, a 128 x 64 tile as 4 x 2
+ * accumulator tiles of 32 x 32 fp32, two K sub-steps of 64 per K tile of 128,
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit scales
+ * (16 MFMAs per wave per K tile).
+ *   operands  device, 32-byte aligned, tdgp_operand_bytes_f8() bytes of E4M3:
+ *             fragment f of lane l is bytes [(f * 512 + l) * 32, +32);
+ *             fragments 0..3 are sub-step 0's A, 4..5 its B, 6..9 sub-step
+ *             1's A, 10..11 its B.
+ *   sink      as above; with every operand byte 0x38 (1.0) each lane writes
+ *             16384 * iters.
+ * Other arguments, returns and ownership as tdgp_mfma_stream. */
+size_t tdgp_operand_bytes_f8(void);
+int tdgp_mfma_stream_f8(const void *operands, int64_t iters, int blocks, float *sink, uint64_t *clocks, void *stream);
+
+/* FLOPs of one tdgp_mfma_stream_f8 call: 2 * 32 * 32 * 64 * 16 * 8 * blocks * iters. */
+double tdgp_flops_f8(int64_t iters, int blocks);
+
 #ifdef __cplusplus
 }
 #endif

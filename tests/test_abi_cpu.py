@@ -253,7 +253,8 @@ def test_probe_library_exports_its_header(tdg):
     import ctypes
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(tdgp_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tdgp_flops", "tdgp_mfma_stream", "tdgp_operand_elems"]
+    assert names == ["tdgp_flops", "tdgp_flops_f8", "tdgp_mfma_stream", "tdgp_mfma_stream_f8", "tdgp_operand_bytes_f8",
+                     "tdgp_operand_elems"]
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
     assert set(names) <= exported
@@ -273,3 +274,13 @@ def test_probe_library_exports_its_header(tdg):
     assert lib.tdgp_mfma_stream(fake, 0, 1, fake, None, None) == 1
     assert lib.tdgp_mfma_stream(fake, 1, 0, fake, None, None) == 1
     assert lib.tdgp_mfma_stream(fake, 1, 65537, fake, None, None) == 1
+    lib.tdgp_operand_bytes_f8.restype = ctypes.c_size_t
+    lib.tdgp_flops_f8.restype = ctypes.c_double
+    lib.tdgp_flops_f8.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.tdgp_mfma_stream_f8.argtypes = lib.tdgp_mfma_stream.argtypes
+    assert lib.tdgp_operand_bytes_f8() == 12 * 512 * 32
+    # 16 MFMAs of 32x32x64 per wave per K tile, 8 waves per workgroup
+    assert lib.tdgp_flops_f8(3, 5) == 2.0 * 32 * 32 * 64 * 16 * 8 * 5 * 3
+    assert lib.tdgp_mfma_stream_f8(None, 1, 1, fake, None, None) == 1
+    assert lib.tdgp_mfma_stream_f8(fake + 16, 1, 1, fake, None, None) == 1  # operands not 32-byte aligned
+    assert lib.tdgp_mfma_stream_f8(fake, 0, 1, fake, None, None) == 1

@@ -1,7 +1,7 @@
-// MFMA ceiling probe (libtdg_probe.so): the per-wave 16x16x32 bf16 MFMA stream
-// of the 256 x 256 GEMM kernel with the operands held in registers, timed to
-// give the rate the matrix cores sustain on a given operand distribution at
-// the clock the chip holds under that load.  Interface and buffer layout are
+// MFMA ceiling probe (libtdg_probe.so): the per-wave MFMA streams of the
+// 256 x 256 GEMM kernels (16x16x32 bf16; scaled 32x32x64 E4M3) with the
+// operands held in registers, timed to give the rate the matrix cores sustain
+// on a given operand distribution at the clock the chip holds under that load.  Interface and buffer layout are
 // described in include/tdg_probe.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,9 +62,80 @@ __global__ __launch_bounds__(kLanes) void mfma_stream_kernel(const bf16x8 *__res
     }
 }
 
+// The 8-bit kernel's per-wave stream: a 128 x 64 wave tile as 4 x 2 tiles of
+// 32 x 32 fp32, two K sub-steps of 64 per K tile of 128, each sub-step taking
+// 4 A and 2 B fragments of 32 bytes (E4M3 both, unit block scales).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kF8Fragments = 12;  // 2 K sub-steps x (4 A + 2 B)
+
+__global__ __launch_bounds__(kLanes) void mfma_stream_f8_kernel(const i32x8 *__restrict__ ops, int64_t iters,
+                                                                float *__restrict__ sink,
+                                                                uint64_t *__restrict__ clocks) {
+    const int t = threadIdx.x;
+    i32x8 a[2][4], b[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[s][i] = ops[(s * 6 + i) * kLanes + t];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[s][j] = ops[(s * 6 + 4 + j) * kLanes + t];
+    }
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[s][j], a[s][i], acc[i][j], 0, 0, 0,
+                                                                               127, 0, 127);
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) sum += acc[i][j][e] + acc[i][j][e + 1];
+    sink[(int64_t)blockIdx.x * kLanes + t] = sum;
+    if (clocks != nullptr && t == 0) {
+        clocks[2 * (int64_t)blockIdx.x] = c1 - c0;
+        clocks[2 * (int64_t)blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t tdgp_operand_bytes_f8(void) { return (size_t)kF8Fragments * kLanes * 32; }
+
+double tdgp_flops_f8(int64_t iters, int blocks) {
+    return 2.0 * 32 * 32 * 64 * 16 * (kLanes / 64) * (double)blocks * (double)iters;
+}
+
+int tdgp_mfma_stream_f8(const void *operands, int64_t iters, int blocks, float *sink, uint64_t *clocks,
+                        void *stream) {
+    if (operands == nullptr || sink == nullptr) return 1;
+    if (((uintptr_t)operands & 31) != 0) return 1;
+    if (iters < 1 || iters > ((int64_t)1 << 31) || blocks < 1 || blocks > 65536) return 1;
+    hipLaunchKernelGGL(mfma_stream_f8_kernel, dim3((unsigned)blocks), dim3(kLanes), 0, (hipStream_t)stream,
+                       static_cast<const i32x8 *>(operands), iters, sink, clocks);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
 
 size_t tdgp_operand_elems(void) { return (size_t)kFragments * kLanes * 8; }
 
