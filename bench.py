@@ -9,21 +9,30 @@ the 8192^3 E4M3 TN products (with and without block scales) are measured
 alongside (their figures are reported under "also").  Inputs are generated on the host, copied to HBM
 before timing, and stay there.
 
-Prints ONE JSON line.  Timing: W untimed warm-up steps; then K timed steps
-between two device synchronisations (wall clock -> ms_per_step and value),
-with a HIP event pair on the stream the kernel runs on around the K
-launches (-> the kernel's average launch duration for the roofline figure:
-the launches run back to back, so the span is their durations plus the
-small gaps between them).  The other workloads are timed the same way over
-at least 50 ms of launches, five times, and report the medians; the
-HBM-bound batched product is also timed with the caches emptied before
-each launch.  "small" gives the per-call cost of the two small workloads
-(host time of a C-ABI call and of the Python wrapper, kernel time, wall
-time per call).  "mfma_ceiling" is the rate of the bf16 kernel's MFMA stream
-with its operands in registers (libtdg_probe.so), on the headline's operand
-distribution and on zeros: the engine clock is power-limited and depends on
-the operand bits, so this, not the published peak, is what the MFMA-bound
-products can reach on random data.
+Prints ONE JSON line.  Timing of the headline workload:
+  * W untimed warm-up steps, then more untimed steps until at least
+    --settle seconds (default 0.3) of back-to-back launches have passed: the
+    engine clock needs tens of milliseconds of load to settle after an idle
+    spell (e.g. while the host generates inputs); the time spent is
+    reported as ``timing.settle_s``;
+  * exactly K timed steps between two device synchronisations (wall clock ->
+    ``ms_per_step`` and ``value``), with a HIP event pair on the kernel's
+    stream around them (-> ``timing.k_steps_kernel_ms``);
+  * the roofline figure (``roofline.kernel_ms``, ``achieved``, ``frac``):
+    the median over 5 blocks of back-to-back launches, each block at least
+    50 ms long, one HIP event pair per block on the kernel's stream (the
+    launches run back to back, so a block's span is their durations plus the
+    small gaps between them).
+The other workloads are timed the same way (settle, then the median of 5
+blocks of at least 50 ms); the HBM-bound batched product is also timed with
+the caches emptied before each launch.  "small" gives the per-call cost of
+the two small workloads (host time of a C-ABI call and of the Python
+wrapper, kernel time, wall time per call).  "mfma_ceiling" is the rate of the
+bf16 kernel's MFMA stream with its operands in registers (libtdg_probe.so),
+on the headline's operand distribution and on zeros: the engine clock is
+power-limited and depends on the operand bits.  "gpu_state" is an amd-smi
+sample taken while launches of the headline workload are still queued (the
+line says whether the queue was still busy when the sample returned).
 """
 import argparse
 import hashlib
@@ -69,7 +78,8 @@ def stored_traffic(workload: str):
 def warm_up(torch, call, steps, min_seconds):
     """`steps` untimed calls, then more until `min_seconds` of wall time
     have passed (the engine clock needs tens of milliseconds of load to
-    settle after an idle spell, e.g. while the host generates inputs)."""
+    settle after an idle spell, e.g. while the host generates inputs).
+    Returns the seconds spent."""
     t0 = time.perf_counter()
     for _ in range(steps):
         call()
@@ -78,6 +88,7 @@ def warm_up(torch, call, steps, min_seconds):
         for _ in range(10):
             call()
         torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def timed_runs(torch, call, stream, steps, repeats=1, min_total_s=0.0):
@@ -106,22 +117,54 @@ def timed_runs(torch, call, stream, steps, repeats=1, min_total_s=0.0):
     return statistics.median(r[0] for r in res), statistics.median(r[1] for r in res)
 
 
-def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_total_s=0.0):
+def _resident(torch, w):
+    """The workload's inputs in HBM and its output buffer."""
     from workloads import TORCH_DTYPE, workload_inputs
     a, b = workload_inputs(w)
     dev = torch.device("cuda:0")
     a, b = a.to(dev), b.to(dev)
-    out_dt = TORCH_DTYPE[w.out_dtype]
     shape = (w.batch, w.M, w.N) if w.batch else (w.M, w.N)
-    c = torch.empty(shape, dtype=out_dt, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    c = torch.empty(shape, dtype=TORCH_DTYPE[w.out_dtype], device=dev)
+    return a, b, c, torch.cuda.current_stream(dev)
+
+
+def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_total_s=0.0):
+    from workloads import TORCH_DTYPE
+    a, b, c, stream = _resident(torch, w)
 
     def call():
         tdg.gemm(a, b, layout=w.layout, out=c)
     warm_up(torch, call, warmup, min_warm_s)
     wall_ms, kernel_ms = timed_runs(torch, call, stream, steps, repeats, min_total_s)
-    cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=out_dt)
+    cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
     return wall_ms, kernel_ms, tdg.tdg_config_name(cfg)
+
+
+def time_headline(tdg, torch, w, steps, warmup, settle_s, blocks=5, block_s=0.05):
+    """The headline leg: warm-up and clock settling, exactly `steps` timed
+    calls (wall clock between two synchronisations, and an event pair on the
+    kernel's stream), then `blocks` blocks of at least `block_s` seconds of
+    back-to-back calls for the roofline figure (median of the blocks)."""
+    import statistics
+    from workloads import TORCH_DTYPE
+    a, b, c, stream = _resident(torch, w)
+
+    def call():
+        tdg.gemm(a, b, layout=w.layout, out=c)
+    settled = warm_up(torch, call, warmup, settle_s)
+    wall_ms, k_kernel_ms = timed_runs(torch, call, stream, steps)
+    out = {"wall_ms": wall_ms, "k_steps_kernel_ms": k_kernel_ms, "settle_s": settled}
+    if blocks > 0:
+        n = max(1, int(block_s * 1e3 / max(k_kernel_ms, 1e-6)) + 1)
+        per_block = [timed_runs(torch, call, stream, n)[1] for _ in range(blocks)]
+        out["kernel_ms"] = statistics.median(per_block)
+        out["block_kernel_ms"] = per_block
+        out["block_calls"] = n
+    else:
+        out["kernel_ms"] = k_kernel_ms
+    cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
+    out["tile_config"] = tdg.tdg_config_name(cfg)
+    return out
 
 
 def time_small(tdg, torch, w, calls=3000):
@@ -226,6 +269,18 @@ def time_f8_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, mi
     return timed_runs(torch, call, stream, steps, repeats, min_total_s)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds_min=10.0):
     """The oracle, unchanged, on a bounded row sample of the same workload:
     evenly spaced output rows (all columns, full K), doubling the row count
@@ -250,6 +305,7 @@ def cpu_baseline(w, seconds_min=10.0):
         nrows *= 2
     flops = 2.0 * len(rows) * w.N * w.K * max(1, w.batch)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "%d of %d output rows%s (all %d columns, full K=%d), %.1f s; value = 2*rows*N*K%s / time"
                       % (len(rows), w.M, " of each of %d problems" % w.batch if w.batch else "", w.N, w.K, dt,
                          "*batch" if w.batch else "")}
@@ -343,21 +399,37 @@ def mfma_ceiling(torch, seconds=0.25):
     return out
 
 
-def gpu_state_under_load(tdg, torch, w, kernel_ms, seconds=1.5):
+def gpu_state_under_load(tdg, torch, w, kernel_ms, seconds=2.0):
     """amd-smi sampled while the GPU runs back-to-back launches of the
-    workload (about `seconds` of them, queued before the sample is taken)."""
-    from workloads import TORCH_DTYPE, workload_inputs
-    a, b = workload_inputs(w)
-    a, b = a.cuda(), b.cuda()
-    c = tdg.gemm(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
-    n = max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
-    for _ in range(n):
-        tdg.gemm(a, b, layout=w.layout, out=c)
-    time.sleep(min(0.5, seconds / 3))
-    state = amd_smi_state()
+    workload: about `seconds` of launches are queued, the sample is taken in
+    a second thread as soon as the first launches run, and an event recorded
+    behind the last launch tells whether the queue was still busy when the
+    sample returned (``under_load``)."""
+    import threading
+    a, b, c, stream = _resident(torch, w)
+    tdg.gemm(a, b, layout=w.layout, out=c)
     torch.cuda.synchronize()
+    n = max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
+    done = torch.cuda.Event()
+    box = {}
+    sampler = threading.Thread(target=lambda: box.update(state=amd_smi_state()))
+    t0 = time.perf_counter()
+    for i in range(n):
+        tdg.gemm(a, b, layout=w.layout, out=c)
+        if i == 50:
+            sampler.start()
+    done.record(stream)
+    if not sampler.is_alive() and "state" not in box:
+        sampler.start()
+    sampler.join()
+    busy = not done.query()
+    t_sample = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    state = box.get("state")
     if state is not None:
-        state["sampled"] = "amd-smi during %d back-to-back launches of %s" % (n, w.name)
+        state["sampled"] = ("amd-smi started after 50 of %d queued back-to-back launches of %s (%.1f s of work); "
+                            "returned after %.2f s" % (n, w.name, n * kernel_ms * 1e-3, t_sample))
+        state["under_load"] = busy
     return state
 
 
@@ -383,6 +455,10 @@ def main():
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true", help="skip the amd-smi clock/temperature sample")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-stream ceiling probe")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed back-to-back launches before timing (clock settling)")
+    ap.add_argument("--blocks", type=int, default=5,
+                    help="blocks of >= 50 ms whose median kernel time gives the roofline figure (0: the K steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -402,7 +478,8 @@ def main():
         calibrate_copy(torch)
         return
     w = WORKLOADS[args.workload]
-    ms, kernel_ms, cfg_name = time_workload(tdg, torch, w, args.steps, args.warmup)
+    h = time_headline(tdg, torch, w, args.steps, args.warmup, args.settle, blocks=args.blocks)
+    ms, kernel_ms, cfg_name = h["wall_ms"], h["kernel_ms"], h["tile_config"]
     flops = w.flops
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
@@ -428,6 +505,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5)},
+        "timing": {"warmup_steps": args.warmup, "settle_s": round(h["settle_s"], 3),
+                   "k_steps_wall_ms": round(ms, 5), "k_steps_kernel_ms": round(h["k_steps_kernel_ms"], 5),
+                   "roofline_kernel_ms": ("median of %d blocks of %d back-to-back launches (>= 50 ms each), "
+                                          "HIP event pair per block on the kernel's stream"
+                                          % (args.blocks, h["block_calls"])) if args.blocks > 0
+                   else "the K timed steps, HIP event pair on the kernel's stream",
+                   "block_kernel_ms": [round(x, 5) for x in h.get("block_kernel_ms", [])]},
     }
     es = 4 if w.out_dtype == "f32" else 2
     alg_bytes = (2 * (w.M * w.K + w.K * w.N) + es * w.M * w.N) * max(1, w.batch)

@@ -20,25 +20,33 @@
  * Layout.  All matrices are row-major.  Leading dimensions are row strides
  * in ELEMENTS: lda >= K; ldb >= N (NN) or ldb >= K (TN); ldc >= N.  Batched
  * calls add element strides between consecutive problems (strideA/B/C); the
- * problems are independent.  Any pointer alignment and any leading dimension
- * are accepted; 16-byte aligned bases with leading dimensions and contiguous
- * extents that are multiples of 8 elements take the vectorised path, the
- * rest a slower predicated path with identical results.
+ * problems are independent.  Every pointer must be aligned to its element
+ * size (2 bytes for A, B and a 16-bit C, 4 bytes for an fp32 C); any leading
+ * dimension is accepted.  16-byte aligned bases with leading dimensions and
+ * contiguous extents that are multiples of 8 elements take the vectorised
+ * path, the rest a slower predicated path with identical results.
  *
  * Ownership.  The caller allocates A, B and C in device memory (HBM) and
  * keeps them alive until the stream work completes.  The library allocates
  * no device memory, keeps no per-call state and never synchronises: each
- * call only validates its arguments and enqueues one kernel on `stream`
- * (a hipStream_t; NULL is the null stream).  C is fully overwritten
- * (alpha = 1, beta = 0) and must not overlap A or B.
+ * call only validates its arguments and enqueues its kernels on `stream`
+ * (a hipStream_t; NULL is the null stream) -- one launch, or two launches
+ * over disjoint parts of C for a single problem whose 256 x 256 output
+ * tiles leave a partial last round on the device's compute units (a band of
+ * whole rounds of 256 x 256 tiles, then the rest in 128 x 128 tiles).  C is
+ * fully overwritten (alpha = 1, beta = 0) and must not overlap A or B.
  *
  * Errors.  Argument errors are reported synchronously, before anything is
  * enqueued, through the return value; tdg_last_error() then describes the
  * cause (thread-local).  Faults inside a kernel surface at the caller's next
  * synchronisation, as for any HIP kernel.
- *   TDG_INVALID_VALUE  negative M, N, K or batch; a NULL pointer with work to
- *                      do; a leading dimension or batch stride too small;
- *                      an unknown dtype or a dtype combination not offered.
+ *   TDG_INVALID_VALUE  negative M, N, K or batch; M, N or K of 2^31 or more;
+ *                      a NULL pointer with work to do; A, B or C not aligned
+ *                      to its element size; a leading dimension too small, a
+ *                      negative batch stride, or a strideC that lets the C
+ *                      matrices of a batch overlap; an unknown dtype or a
+ *                      dtype combination not offered; more than 2^31 - 1
+ *                      output tiles of 64 x 64.
  *   TDG_NOT_SUPPORTED  the current device is not gfx950.
  *   TDG_LAUNCH_FAILED  the kernel launch was rejected by the HIP runtime.
  * Degenerate sizes: M == 0, N == 0 or batch == 0 do nothing and succeed;
@@ -173,6 +181,15 @@ tdg_status tdg_gemm(int transa, int transb, int transc, int64_t M, int64_t N, in
  * vectorised kernels need none.  Also valid for tdg_gemm with any
  * transa, transb, transc (the tile counts do not depend on them). */
 size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int64_t batch, int num_cus);
+
+/* An upper bound of tdg_gemm_workspace_size over every problem, on a device
+ * with `num_cus` compute units (0: the current device; 0 is returned when
+ * no gfx950 device is current): a workspace of this size serves any call,
+ * so a caller can allocate one per stream once and never replace it (for
+ * instance when calls are captured in a HIP graph, whose replays keep
+ * using the pointer they were captured with).  A graph replay and an eager
+ * call that share a workspace must not overlap in time. */
+size_t tdg_gemm_workspace_bound(int num_cus);
 
 /* Autotuning (tile selection by measurement).  Times every tile
  * configuration that can serve these arguments, and the library's own

@@ -165,6 +165,20 @@ def test_split_k_workspace_plan(tdg):
     assert ws(0, 0, 8, 8) == 0 and ws(0, 8, 8, 0) == 0 and ws(2, 64, 64, 64) == 0
 
 
+def test_split_k_workspace_bound(tdg):
+    """The bound serves every call: at most one 128 x 128 fp32 partial per CU
+    after the counter block, and at least every size the plan asks for."""
+    tile = 128 * 128 * 4
+    for cus in (64, 80, 256, 304):
+        bound = tdg.tdg_gemm_workspace_bound(cus)
+        assert bound == cus * tile + (cus * 4 + 255) // 256 * 256
+        for transb in (0, 1):
+            for M, N, K in ((1024, 1024, 16384), (300, 520, 16384), (512, 256, 16384), (128, 128, 1 << 20),
+                            (130, 1000, 65536), (4000, 100, 100000), (1, 1, 1 << 24)):
+                for batch in (1, 2, 3):
+                    assert tdg.tdg_gemm_workspace_size(transb, M, N, K, batch, cus) <= bound
+
+
 def test_autotune_argument_checks(tdg):
     import ctypes
     best = ctypes.c_int(7)

@@ -1,0 +1,208 @@
+"""GPU parity of the four product entry points of ``include/tdg.h`` called as
+they are declared: ``tdg_gemm_nn``, ``tdg_gemm_tn``, ``tdg_gemm_nn_batched``
+and ``tdg_gemm_tn_batched``, through ctypes with raw device pointers, element
+leading dimensions and the stream handle -- no tensor-level wrapper in
+between.  Each result is compared with the CPU oracle on the same bit
+patterns: bit for bit on integer inputs, within the stated tolerance on
+random inputs.  C is written into the middle of a guard-banded buffer whose
+row padding and surrounding bands hold a sentinel, so a store outside C shows.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from parity import OUT_TORCH, check_exact, check_tol, ref_gemm
+from workloads import WORKLOADS, make_inputs, sample_rows, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+CODE = {"f16": 0, "bf16": 1, "f32": 2}
+SENTINEL = -7.0          # exactly representable in every output type, never a product here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_dense_gemm_03_amd as t
+    return t._binding.lib
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+def framed_c(rows, cols, ldc, out_dtype, batch=0, stride=None, guard=4096):
+    """A device buffer holding C (rows x cols, row stride ldc; `batch`
+    matrices `stride` elements apart) between guard bands, filled with the
+    sentinel.  Returns (buffer, element offset of C[0, 0], stride)."""
+    nb = max(batch, 1)
+    if stride is None:
+        stride = rows * ldc
+    n = guard + (nb - 1) * stride + (rows - 1) * ldc + cols + guard
+    buf = torch.full((n,), SENTINEL, dtype=OUT_TORCH[out_dtype], device="cuda")
+    return buf, guard, stride
+
+
+def view_c(buf, off, rows, cols, ldc, batch=0, stride=0):
+    if batch:
+        return buf.as_strided((batch, rows, cols), (stride, ldc, 1), off)
+    return buf.as_strided((rows, cols), (ldc, 1), off)
+
+
+def check_frame(buf, off, rows, cols, ldc, batch=0, stride=0):
+    """Every element of the buffer outside C still holds the sentinel."""
+    host = buf.float().cpu()
+    mask = torch.ones_like(host, dtype=torch.bool)
+    for b in range(max(batch, 1)):
+        base = off + b * stride
+        for r in range(rows):
+            mask[base + r * ldc: base + r * ldc + cols] = False
+    outside = host[mask]
+    assert bool((outside == SENTINEL).all()), "%d elements outside C were written" % int((outside != SENTINEL).sum())
+
+
+def padded(t, ld):
+    """The matrix t (rows x cols, or batch x rows x cols) on the device with
+    row stride ld (elements), padding filled with NaN."""
+    rows, cols = t.shape[-2], t.shape[-1]
+    lead = t.shape[:-2]
+    store = torch.full(lead + (rows, ld), float("nan"), dtype=t.dtype)
+    store[..., :cols] = t
+    return store.cuda()
+
+
+def stream_ptr():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def call_single(lib, layout, a, b, M, N, K, in_dtype, out_dtype, lda, ldb, ldc):
+    ad, bd = padded(a, lda), padded(b, ldb)
+    buf, off, _ = framed_c(M, N, ldc, out_dtype)
+    es = buf.element_size()
+    fn = lib.tdg_gemm_nn if layout == "nn" else lib.tdg_gemm_tn
+    st = fn(M, N, K, ad.data_ptr(), lda, bd.data_ptr(), ldb, buf.data_ptr() + off * es, ldc,
+            CODE[in_dtype], CODE[out_dtype], stream_ptr())
+    assert st == 0, lib.tdg_last_error().decode()
+    torch.cuda.synchronize()
+    check_frame(buf, off, M, N, ldc)
+    return view_c(buf, off, M, N, ldc).cpu()
+
+
+def call_batched(lib, layout, a, b, M, N, K, batch, in_dtype, out_dtype, lda, ldb, ldc, pad_c=0):
+    ad, bd = padded(a, lda), padded(b, ldb)
+    sA = ad.stride(0)
+    sB = bd.stride(0)
+    sC = M * ldc + pad_c
+    buf, off, _ = framed_c(M, N, ldc, out_dtype, batch=batch, stride=sC)
+    es = buf.element_size()
+    fn = lib.tdg_gemm_nn_batched if layout == "nn" else lib.tdg_gemm_tn_batched
+    st = fn(M, N, K, ad.data_ptr(), lda, sA, bd.data_ptr(), ldb, sB, buf.data_ptr() + off * es, ldc, sC, batch,
+            CODE[in_dtype], CODE[out_dtype], stream_ptr())
+    assert st == 0, lib.tdg_last_error().decode()
+    torch.cuda.synchronize()
+    check_frame(buf, off, M, N, ldc, batch, sC)
+    return view_c(buf, off, M, N, ldc, batch, sC).cpu()
+
+
+def test_nn_worked_example_whole(lib):
+    """The worked 128 x 192 . 192 x 256 fp16 product through tdg_gemm_nn:
+    random inputs within tolerance, integer inputs bit for bit."""
+    w = WORKLOADS["worked_128x256x192"]
+    announce("tdg_gemm_nn", w.name)
+    a, b = workload_inputs(w)
+    c = call_single(lib, "nn", a, b, w.M, w.N, w.K, "f16", "f16", w.K, w.N, w.N)
+    check_tol(c, ref_gemm(a, b, "f16", "nn"), "f16", w.K, "tdg_gemm_nn worked")
+    ai, bi = make_inputs(w.M, w.N, w.K, "nn", "f16", "ints", seed=w.seed + 1000)
+    ci = call_single(lib, "nn", ai, bi, w.M, w.N, w.K, "f16", "f16", w.K, w.N, w.N)
+    check_exact(ci, ref_gemm(ai, bi, "f16", "nn"), "f16", "tdg_gemm_nn worked ints")
+
+
+def test_tn_exact_1024(lib):
+    """The 1024^3 TN exactness product through tdg_gemm_tn, fp32 output."""
+    w = WORKLOADS["tn_exact_1024"]
+    announce("tdg_gemm_tn", w.name)
+    a, b = workload_inputs(w)
+    c = call_single(lib, "tn", a, b, w.M, w.N, w.K, "f16", "f32", w.K, w.K, w.N)
+    check_exact(c, ref_gemm(a, b, "f16", "tn"), "f32", "tdg_gemm_tn 1024^3")
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
+def test_tn_batched_exact(lib, in_dtype, out_dtype):
+    """A small batched TN product (5 problems of 200 x 136 x 72, padded rows,
+    C matrices with a gap between them) through tdg_gemm_tn_batched."""
+    M, N, K, batch = 200, 136, 72, 5
+    announce("tdg_gemm_tn_batched", M, N, K, batch, in_dtype, out_dtype)
+    a, b = make_inputs(M, N, K, "tn", in_dtype, "ints", seed=71, batch=batch)
+    c = call_batched(lib, "tn", a, b, M, N, K, batch, in_dtype, out_dtype, lda=K + 8, ldb=K + 16, ldc=N + 8, pad_c=24)
+    check_exact(c, ref_gemm(a, b, in_dtype, "tn"), out_dtype, "tdg_gemm_tn_batched")
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f16"), ("bf16", "f32")])
+def test_nn_batched_exact(lib, in_dtype, out_dtype):
+    M, N, K, batch = 96, 264, 136, 4
+    announce("tdg_gemm_nn_batched", M, N, K, batch, in_dtype, out_dtype)
+    a, b = make_inputs(M, N, K, "nn", in_dtype, "ints", seed=72, batch=batch)
+    c = call_batched(lib, "nn", a, b, M, N, K, batch, in_dtype, out_dtype, lda=K, ldb=N + 8, ldc=N)
+    check_exact(c, ref_gemm(a, b, in_dtype, "nn"), out_dtype, "tdg_gemm_nn_batched")
+
+
+# Ragged shapes: odd sizes and leading dimensions (the predicated path), and
+# the 4095 x 5000 x 3000 product, which the library serves as a band of
+# 256 x 256 tiles plus a 128 x 128 remainder (two launches).
+RAGGED_SINGLE = [(65, 97, 130, 131, 99, 101), (4095, 5000, 3000, 3000, None, 5000)]
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", RAGGED_SINGLE)
+def test_single_ragged(lib, layout, M, N, K, lda, ldb, ldc):
+    if ldb is None:
+        ldb = N if layout == "nn" else K
+    announce("tdg_gemm_%s ragged" % layout, M, N, K)
+    a, b = make_inputs(M, N, K, layout, "f16", "uniform", seed=M + N + K)
+    c = call_single(lib, layout, a, b, M, N, K, "f16", "f16", lda, ldb, ldc)
+    if M * N * K <= 2 ** 26:
+        check_tol(c, ref_gemm(a, b, "f16", layout), "f16", K, "ragged")
+        ai, bi = make_inputs(M, N, K, layout, "f16", "ints", seed=M + N + K + 1)
+        ci = call_single(lib, layout, ai, bi, M, N, K, "f16", "f32", lda, ldb, ldc)
+        check_exact(ci, ref_gemm(ai, bi, "f16", layout), "f32", "ragged ints")
+        return
+    rows = sample_rows(M)
+    check_tol(c[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f16", K, "ragged cut")
+    ai, bi = make_inputs(M, N, K, layout, "f16", "ints", seed=M + N + K + 1)
+    ci = call_single(lib, layout, ai, bi, M, N, K, "f16", "f32", lda, ldb, ldc)
+    check_exact(ci[rows], ref_gemm(ai, bi, "f16", layout, rows=rows), "f32", "ragged cut ints")
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_batched_ragged(lib, layout):
+    M, N, K, batch = 65, 97, 130, 3
+    announce("tdg_gemm_%s_batched ragged" % layout, M, N, K, batch)
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=73, batch=batch)
+    ldb = N + 3 if layout == "nn" else K + 5
+    c = call_batched(lib, layout, a, b, M, N, K, batch, "bf16", "f32", lda=K + 1, ldb=ldb, ldc=N + 2, pad_c=7)
+    check_exact(c, ref_gemm(a, b, "bf16", layout), "f32", "batched ragged")
+
+
+def test_degenerate_sizes(lib):
+    """K = 0 writes zeros (the empty sum) and nothing else; M = 0 and batch = 0
+    write nothing."""
+    announce("degenerate")
+    buf, off, _ = framed_c(33, 40, 48, "f16")
+    es = buf.element_size()
+    st = lib.tdg_gemm_nn(33, 40, 0, None, 1, None, 40, buf.data_ptr() + off * es, 48, 0, 0, stream_ptr())
+    assert st == 0, lib.tdg_last_error().decode()
+    torch.cuda.synchronize()
+    check_frame(buf, off, 33, 40, 48)
+    assert bool((view_c(buf, off, 33, 40, 48).float().cpu() == 0).all())
+    buf2, off2, _ = framed_c(4, 4, 4, "f32")
+    st = lib.tdg_gemm_tn_batched(0, 4, 8, None, 8, 0, None, 8, 0, buf2.data_ptr(), 4, 16, 3, 0, 2, stream_ptr())
+    assert st == 0
+    st = lib.tdg_gemm_nn_batched(4, 4, 8, None, 8, 32, None, 4, 32, buf2.data_ptr(), 4, 16, 0, 0, 2, stream_ptr())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert bool((buf2.cpu() == SENTINEL).all())

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     tdg_gemm_nn_batched,
     tdg_gemm_tn,
     tdg_gemm_tn_batched,
+    tdg_gemm_workspace_bound,
     tdg_gemm_workspace_size,
     tdg_gemm_ws,
     tdg_last_error,

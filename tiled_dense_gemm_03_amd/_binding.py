@@ -38,6 +38,7 @@ _SIG = {
     "tdg_gemm_ws": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                            _int, _int, _vp, _sz, _vp]),
     "tdg_gemm_workspace_size": (_sz, [_int, _i64, _i64, _i64, _i64, _int]),
+    "tdg_gemm_workspace_bound": (_sz, [_int]),
     "tdg_gemm": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                         _int, _int, _vp, _sz, _vp]),
     "tdg_autotune": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
@@ -103,6 +104,10 @@ def tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, 
 
 def tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus):
     return lib.tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus)
+
+
+def tdg_gemm_workspace_bound(num_cus):
+    return lib.tdg_gemm_workspace_bound(num_cus)
 
 
 def tdg_autotune(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,

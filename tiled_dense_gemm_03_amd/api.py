@@ -74,7 +74,11 @@ def select_config(a, b, layout="nn", out_dtype=None):
 
 # Split-K workspaces, one per (device, stream) so that calls that may run at
 # the same time never share one; zero-filled once by torch, kept zero-filled by
-# the library.  Replaced by a larger one when a call needs more.
+# the library.  Each is allocated once, at the library's bound for the device
+# (tdg_gemm_workspace_bound: enough for any call), and never replaced or
+# freed: a HIP graph captured with one keeps using its address on every
+# replay.  A replay and an eager call on the same stream's workspace must not
+# overlap in time (torch replays a graph on the stream it is replayed from).
 _workspaces = {}
 # Workspace bytes the library asks for, per problem (the answer depends only
 # on the sizes and the device's compute-unit count).
@@ -82,11 +86,17 @@ _ws_need = {}
 
 
 def _workspace(device, stream, nbytes):
-    key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, stream)
     ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+    if ws is None:
+        with torch.cuda.device(index):
+            bound = _b.tdg_gemm_workspace_bound(0)
+        ws = torch.zeros(max(bound, nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
+    if ws.numel() < nbytes:
+        raise RuntimeError("split-K workspace of %d bytes is below the %d bytes a call asks for "
+                           "(the library's bound)" % (ws.numel(), nbytes))
     return ws
 
 

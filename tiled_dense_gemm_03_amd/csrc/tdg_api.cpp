@@ -1,9 +1,11 @@
 // tdg_api.cpp -- the C ABI of the tiled dense GEMM library (host side).
 //
-// Validates arguments, picks a tile configuration and enqueues exactly one
-// kernel on the caller's stream.  No allocation, no synchronisation, no
-// per-call state beyond the thread-local error text and a per-device
-// architecture check made once.
+// Validates arguments, picks a tile configuration and enqueues its kernels
+// on the caller's stream: one launch, or two over disjoint parts of C when a
+// single problem's 256 x 256 tiles leave a partial last round (plan_retile).
+// No allocation, no synchronisation, no per-call state beyond the
+// thread-local error text, a per-device architecture check made once and
+// the autotuning table.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -178,6 +180,13 @@ size_t split_ws_bytes(const Config &cf, const SplitPlan &pl, int64_t cus) {
     return split_flag_bytes(cus) + (size_t)pl.sk_tiles * pl.split * cf.bm * cf.bn * 4;
 }
 
+// The largest workspace any call needs on a device with `cus` compute units.
+// Only the automatic choice splits K, and only for problems with fewer tiles
+// than CUs, which it serves with 128 x 128 tiles (256 x 256 tiles are chosen
+// only for at least one tile per CU); plan_split gives at most `cus` slices
+// in all (rem * floor(cus / rem) <= cus).
+size_t split_ws_bound(int64_t cus) { return split_flag_bytes(cus) + (size_t)cus * 128 * 128 * 4; }
+
 // Whether a split schedule is worth taking for a problem below one round of
 // 256 x 256 tiles: it must give at least half the chip a work item.
 bool split_pays(const SplitPlan &pl, int64_t cus) {
@@ -308,11 +317,13 @@ tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int6
         if (!split_pays(pl, cus)) pl = SplitPlan{tiles, 0, 1};
     }
     const size_t need = split_ws_bytes(cf, pl, cus);
-    if (need > ws_bytes)
+    if (need > split_ws_bound(cus)) pl = SplitPlan{tiles, 0, 1};   // (not reached: see split_ws_bound)
+    if (split_ws_bytes(cf, pl, cus) > ws_bytes)
         return fail(TDG_INVALID_VALUE, "workspace of %zu bytes is smaller than the %zu bytes this call needs", ws_bytes,
-                    need);
-    a.ws_flags = need ? static_cast<int *>(ws) : nullptr;
-    a.ws = need ? reinterpret_cast<float *>(static_cast<char *>(ws) + split_flag_bytes(cus)) : nullptr;
+                    split_ws_bytes(cf, pl, cus));
+    const bool split = pl.split >= 2;
+    a.ws_flags = split ? static_cast<int *>(ws) : nullptr;
+    a.ws = split ? reinterpret_cast<float *>(static_cast<char *>(ws) + split_flag_bytes(cus)) : nullptr;
     a.dp_tiles = (int)pl.dp_tiles;
     a.sk_split = pl.split;
     const int64_t grid = pl.dp_tiles + pl.sk_tiles * pl.split;
@@ -670,6 +681,12 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
     const tdg::SplitPlan pl = tdg::plan_split(tiles, tdg::cdiv(K, cf.bk), cus);
     if (!tdg::split_pays(pl, cus)) return 0;
     return tdg::split_ws_bytes(cf, pl, cus);
+}
+
+size_t tdg_gemm_workspace_bound(int num_cus) {
+    int cus = num_cus;
+    if (cus <= 0 && tdg::check_device(&cus) != TDG_SUCCESS) return 0;
+    return tdg::split_ws_bound(cus);
 }
 
 tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
