@@ -257,7 +257,7 @@ def test_f8_degenerate_sizes_succeed_without_a_device(tdg):
     assert _f8_call(tdg, N=0, A=None, B=None, C=None) == tdg.TDG_SUCCESS
 
 
-PROBE_HEADER = os.path.join(ROOT, "include", "tdg_probe.h")
+PROBE_HEADER = os.path.join(ROOT, "tiled_dense_gemm_03_amd", "probe", "tdg_probe.h")
 PROBE_LIB = os.path.join(ROOT, "tiled_dense_gemm_03_amd", "libtdg_probe.so")
 
 
@@ -267,8 +267,8 @@ def test_probe_library_exports_its_header(tdg):
     import ctypes
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(tdgp_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tdgp_flops", "tdgp_flops_f8", "tdgp_mfma_stream", "tdgp_mfma_stream_f8", "tdgp_operand_bytes_f8",
-                     "tdgp_operand_elems"]
+    assert names == ["tdgp_flops", "tdgp_flops_f8", "tdgp_mfma_lanes", "tdgp_mfma_stream", "tdgp_mfma_stream_f8",
+                     "tdgp_operand_bytes_f8", "tdgp_operand_elems"]
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
     assert set(names) <= exported
@@ -298,3 +298,10 @@ def test_probe_library_exports_its_header(tdg):
     assert lib.tdgp_mfma_stream_f8(None, 1, 1, fake, None, None) == 1
     assert lib.tdgp_mfma_stream_f8(fake + 16, 1, 1, fake, None, None) == 1  # operands not 32-byte aligned
     assert lib.tdgp_mfma_stream_f8(fake, 0, 1, fake, None, None) == 1
+    lib.tdgp_mfma_lanes.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tdgp_mfma_lanes(5, fake, fake, None, None, fake, None) == 1          # no such kind
+    assert lib.tdgp_mfma_lanes(-1, fake, fake, None, None, fake, None) == 1
+    assert lib.tdgp_mfma_lanes(0, fake + 16, fake, None, None, fake, None) == 1     # X not 32-byte aligned
+    assert lib.tdgp_mfma_lanes(0, fake, None, None, None, fake, None) == 1
+    assert lib.tdgp_mfma_lanes(4, fake, fake, None, fake, fake, None) == 1          # scaled kind without scales

@@ -154,14 +154,14 @@ def test_nn_batched_exact(lib, in_dtype, out_dtype):
 # Ragged shapes: odd sizes and leading dimensions (the predicated path), and
 # the 4095 x 5000 x 3000 product, which the library serves as a band of
 # 256 x 256 tiles plus a 128 x 128 remainder (two launches).
-RAGGED_SINGLE = [(65, 97, 130, 131, 99, 101), (4095, 5000, 3000, 3000, None, 5000)]
+# (M, N, K, lda, extra row padding of B, ldc)
+RAGGED_SINGLE = [(65, 97, 130, 131, 3, 101), (4095, 5000, 3000, 3000, 0, 5000)]
 
 
 @pytest.mark.parametrize("layout", ["nn", "tn"])
-@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", RAGGED_SINGLE)
-def test_single_ragged(lib, layout, M, N, K, lda, ldb, ldc):
-    if ldb is None:
-        ldb = N if layout == "nn" else K
+@pytest.mark.parametrize("M,N,K,lda,bpad,ldc", RAGGED_SINGLE)
+def test_single_ragged(lib, layout, M, N, K, lda, bpad, ldc):
+    ldb = (N if layout == "nn" else K) + bpad
     announce("tdg_gemm_%s ragged" % layout, M, N, K)
     a, b = make_inputs(M, N, K, layout, "f16", "uniform", seed=M + N + K)
     c = call_single(lib, layout, a, b, M, N, K, "f16", "f16", lda, ldb, ldc)

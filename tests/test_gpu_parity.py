@@ -125,6 +125,38 @@ def test_every_config_integer_exact(tdg, layout, in_dtype, out_dtype):
                             "%s %s %dx%dx%d" % (layout, tdg.tdg_config_name(cfg), M, N, K))
 
 
+# The primer's tail-test plan (NineToothed GEMM primer, section 5, last
+# paragraph): M, N and K tails each tested on their own and together,
+# including several full K tiles followed by a tail.  Edge values around the
+# tile and MFMA sizes; a seeded sample of (M, N, K) per configuration, plus
+# the three one-dimension-ragged cases at the largest edge.
+TAIL_VALUES = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _tail_shapes(cfg, layout, vec, count=10):
+    import random
+    rng = random.Random(1000 * cfg + (layout == "tn"))
+    ok = (lambda v: v % 8 == 0) if vec else (lambda v: True)
+    ks = [v for v in TAIL_VALUES if ok(v)]
+    ns = [v for v in TAIL_VALUES if ok(v)] if (vec and layout == "nn") else TAIL_VALUES
+    shapes = [(257, max(ns), max(ks)), (max(TAIL_VALUES), 17 if 17 in ns else 16, max(ks)),
+              (255, max(ns), 129 if 129 in ks else 136)]
+    shapes += [(rng.choice(TAIL_VALUES), rng.choice(ns), rng.choice(ks)) for _ in range(count)]
+    return shapes
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_tail_sweep_every_config_exact(tdg, layout):
+    for cfg in range(tdg.tdg_num_configs()):
+        name = tdg.tdg_config_name(cfg)
+        vec = not name.endswith("_pred")
+        for (M, N, K) in _tail_shapes(cfg, layout, vec):
+            announce("tail sweep", layout, name, M, N, K)
+            a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M * 131 + N * 7 + K + cfg)
+            c = gpu_gemm(tdg, a, b, layout, "f32", config=cfg)
+            check_exact(c, ref_gemm(a, b, "bf16", layout), "f32", "%s %s %dx%dx%d" % (layout, name, M, N, K))
+
+
 @pytest.mark.parametrize("layout", ["nn", "tn"])
 def test_every_config_random_tolerance(tdg, layout):
     for cfg in range(tdg.tdg_num_configs()):

@@ -2,11 +2,11 @@
 // 256 x 256 GEMM kernels (16x16x32 bf16; scaled 32x32x64 E4M3) with the
 // operands held in registers, timed to give the rate the matrix cores sustain
 // on a given operand distribution at the clock the chip holds under that load.  Interface and buffer layout are
-// described in include/tdg_probe.h.
+// described in tdg_probe.h beside this file.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/tdg_probe.h"
+#include "tdg_probe.h"
 
 namespace {
 
@@ -116,9 +116,72 @@ __global__ __launch_bounds__(kLanes) void mfma_stream_f8_kernel(const i32x8 *__r
     }
 }
 
+// One MFMA of each kind the kernels use, on one wave, for pinning the lane
+// maps: lane l passes its 32-byte X and Y operand slots (the first 16 bytes
+// for the 16-bit kinds) and, for the scaled kind, its scale bytes; every
+// accumulator register starts at zero and is written to d[l * 16 + r].
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+
+template <int KIND>
+__global__ __launch_bounds__(64) void mfma_lanes_kernel(const u32x8 *__restrict__ x, const u32x8 *__restrict__ y,
+                                                        const uint8_t *__restrict__ sx,
+                                                        const uint8_t *__restrict__ sy, float *__restrict__ d) {
+    const int l = threadIdx.x;
+    const u32x8 xv = x[l], yv = y[l];
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v x4 = {xv[0], xv[1], xv[2], xv[3]}, y4 = {yv[0], yv[1], yv[2], yv[3]};
+    if constexpr (KIND <= 1) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KIND == 0)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x4), __builtin_bit_cast(f16x8, y4),
+                                                         acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x4),
+                                                          __builtin_bit_cast(bf16x8, y4), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[l * 16 + r] = acc[r];
+    } else {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        if constexpr (KIND == 2)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x4), __builtin_bit_cast(f16x8, y4),
+                                                         acc, 0, 0, 0);
+        else if constexpr (KIND == 3)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x4),
+                                                          __builtin_bit_cast(bf16x8, y4), acc, 0, 0, 0);
+        else
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, xv),
+                                                                 __builtin_bit_cast(i32x8, yv), acc, 0, 0, 0,
+                                                                 (int)sx[l], 0, (int)sy[l]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) d[l * 16 + r] = acc[r];
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int tdgp_mfma_lanes(int kind, const void *x, const void *y, const void *scale_x, const void *scale_y, float *d,
+                    void *stream) {
+    if (x == nullptr || y == nullptr || d == nullptr) return 1;
+    if ((((uintptr_t)x | (uintptr_t)y) & 31) != 0 || ((uintptr_t)d & 3) != 0) return 1;
+    if (kind == 4 && (scale_x == nullptr || scale_y == nullptr)) return 1;
+    const u32x8 *xv = static_cast<const u32x8 *>(x), *yv = static_cast<const u32x8 *>(y);
+    const uint8_t *sx = static_cast<const uint8_t *>(scale_x), *sy = static_cast<const uint8_t *>(scale_y);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(mfma_lanes_kernel<0>, dim3(1), dim3(64), 0, s, xv, yv, sx, sy, d); break;
+    case 1: hipLaunchKernelGGL(mfma_lanes_kernel<1>, dim3(1), dim3(64), 0, s, xv, yv, sx, sy, d); break;
+    case 2: hipLaunchKernelGGL(mfma_lanes_kernel<2>, dim3(1), dim3(64), 0, s, xv, yv, sx, sy, d); break;
+    case 3: hipLaunchKernelGGL(mfma_lanes_kernel<3>, dim3(1), dim3(64), 0, s, xv, yv, sx, sy, d); break;
+    case 4: hipLaunchKernelGGL(mfma_lanes_kernel<4>, dim3(1), dim3(64), 0, s, xv, yv, sx, sy, d); break;
+    default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+}
 
 size_t tdgp_operand_bytes_f8(void) { return (size_t)kF8Fragments * kLanes * 32; }
 

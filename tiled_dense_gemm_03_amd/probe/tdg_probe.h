@@ -74,6 +74,25 @@ int tdgp_mfma_stream_f8(const void *operands, int64_t iters, int blocks, float *
 /* FLOPs of one tdgp_mfma_stream_f8 call: 2 * 32 * 32 * 64 * 16 * 8 * blocks * iters. */
 double tdgp_flops_f8(int64_t iters, int blocks);
 
+/* One MFMA of the given kind on one wave, every accumulator register
+ * starting at zero, for checking the operand and result lane maps the
+ * kernels are written against:
+ *   kind 0 v_mfma_f32_16x16x32_f16     1 v_mfma_f32_16x16x32_bf16
+ *   kind 2 v_mfma_f32_32x32x16_f16     3 v_mfma_f32_32x32x16_bf16
+ *   kind 4 v_mfma_scale_f32_32x32x64_f8f6f4, both operands E4M3, scale
+ *          operand byte 0 of each lane's scale (op_sel 0)
+ *   x, y     device, 32-byte aligned, 64 x 32 bytes: lane l's X (first
+ *            source) and Y (second source) operand registers are bytes
+ *            [32 l, 32 l + 32) (the 16-bit kinds use the first 16 of them)
+ *   scale_x, scale_y  device, 64 bytes each (kind 4 only, else may be NULL):
+ *            lane l's E8M0 scale byte for X and for Y
+ *   d        device fp32[64 * 16]: lane l's accumulator register r at
+ *            d[16 l + r] (r < 4 for the 16 x 16 kinds; the rest untouched)
+ * Returns 0, 1 for a bad argument (nothing enqueued), 3 when the launch was
+ * rejected.  Enqueued on `stream`; nothing allocated, nothing synchronised. */
+int tdgp_mfma_lanes(int kind, const void *x, const void *y, const void *scale_x, const void *scale_y, float *d,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif
