@@ -191,6 +191,30 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
  * call that share a workspace must not overlap in time. */
 size_t tdg_gemm_workspace_bound(int num_cus);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation.  The same
+ * product as tdg_gemm (same arguments, storage orders, checks and results,
+ * bit for bit), with the split-K workspace taken from a scratch array that is
+ * part of the library's device code: TDG_NOALLOC_SCRATCH_BYTES on every GPU
+ * the library runs on, held from the library's load until the process ends.
+ * The call allocates nothing and frees nothing.
+ *   - Every call on one GPU uses that GPU's array, which keeps what the last
+ *     call left (its arrival counters back at zero).  Calls that may overlap
+ *     in time on one GPU -- on several streams, from several threads, or a
+ *     graph replay beside an eager call -- race on the array and must not be
+ *     issued; serialise them (one stream) or use tdg_gemm with a workspace
+ *     per stream.
+ *   - TDG_INVALID_VALUE when the device's split-K schedule could need more
+ *     than TDG_NOALLOC_SCRATCH_BYTES (a device with more than 256 compute
+ *     units), besides tdg_gemm's own errors. */
+#define TDG_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u + 4096u)
+tdg_status tdg_gemm_noalloc(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda, int64_t strideA,
+                            const void *B, int64_t ldb, int64_t strideB,
+                            void *C, int64_t ldc, int64_t strideC,
+                            int64_t batch,
+                            tdg_dtype ab_type, tdg_dtype c_type, void *stream);
+
 /* Autotuning (tile selection by measurement).  Times every tile
  * configuration that can serve these arguments, and the library's own
  * schedule, `reps` calls each on the caller's buffers and stream, and records

@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     tdg_gemm_f8,
     tdg_gemm_nn,
     tdg_gemm_nn_batched,
+    tdg_gemm_noalloc,
     tdg_gemm_tn,
     tdg_gemm_tn_batched,
     tdg_gemm_workspace_bound,

@@ -41,6 +41,8 @@ _SIG = {
     "tdg_gemm_workspace_bound": (_sz, [_int]),
     "tdg_gemm": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                         _int, _int, _vp, _sz, _vp]),
+    "tdg_gemm_noalloc": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
+                                _i64, _i64, _int, _int, _vp]),
     "tdg_autotune": (_int, [_int, _int, _int, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                             _i64, _int, _int, _vp, _sz, _int, ctypes.POINTER(_int), _vp]),
     "tdg_autotune_clear": (None, []),
@@ -100,6 +102,12 @@ def tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, 
              c_type, workspace, workspace_bytes, stream):
     return lib.tdg_gemm(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
                         ab_type, c_type, workspace, workspace_bytes, stream)
+
+
+def tdg_gemm_noalloc(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                     ab_type, c_type, stream):
+    return lib.tdg_gemm_noalloc(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                                batch, ab_type, c_type, stream)
 
 
 def tdg_gemm_workspace_size(transb, M, N, K, batch, num_cus):

@@ -605,10 +605,64 @@ tdg_status run_f8(int transc, int64_t M, int64_t N, int64_t K, const void *A, in
     return TDG_SUCCESS;
 }
 
+// ---- allocation-free calls: a fixed split-K scratch area per GPU ----
+//
+// The split-K workspace of tdg_gemm_noalloc: one array per GPU, part of the
+// library's device code, so it exists from the library's load until the
+// process ends and no call allocates.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in for the device symbol):
+// the address on each device comes from hipGetSymbolAddress, once per device,
+// with that device current.  Layout as any workspace: the arrival counters
+// first (zero between calls: the loader zero-fills the array and every
+// merging slice puts its counter back), then the fp32 partial tiles.
+constexpr size_t kScratchBytes = TDG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (nullptr: not looked up yet)
+
+// The scratch array's address on the current device `dev`.
+tdg_status scratch_of(int dev, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(TDG_LAUNCH_FAILED, "cannot find the scratch array on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TDG_SUCCESS;
+}
+
 }  // namespace
 }  // namespace tdg
 
 extern "C" {
+
+tdg_status tdg_gemm_noalloc(int transa, int transb, int transc, int64_t M, int64_t N, int64_t K, const void *A,
+                            int64_t lda, int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C,
+                            int64_t ldc, int64_t strideC, int64_t batch, tdg_dtype ab_type, tdg_dtype c_type,
+                            void *stream) {
+    using namespace tdg;
+    g_err[0] = '\0';
+    tdg_status st = validate(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                             batch, ab_type, c_type);
+    if (st != TDG_SUCCESS) return st;
+    if (M == 0 || N == 0 || batch == 0) return TDG_SUCCESS;
+    int cus = 0, dev = 0;
+    st = check_device(&cus, &dev);
+    if (st != TDG_SUCCESS) return st;
+    if (split_ws_bound(cus) > kScratchBytes)
+        return fail(TDG_INVALID_VALUE,
+                    "the split-K schedule of a %d-CU device may need %zu bytes, more than the %zu-byte scratch array",
+                    cus, split_ws_bound(cus), kScratchBytes);
+    void *ws = nullptr;
+    st = scratch_of(dev, &ws);
+    if (st != TDG_SUCCESS) return st;
+    return run(transa, transb, transc, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch, ab_type,
+               c_type, -1, stream, ws, kScratchBytes);
+}
 
 tdg_status tdg_gemm_f8(int transc, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, tdg_dtype a_type,
                        const void *B, int64_t ldb, tdg_dtype b_type, const void *block_scale_a, int64_t ld_bsa,
