@@ -140,17 +140,18 @@ def time_workload(tdg, torch, w, steps, warmup, min_warm_s=0.0, repeats=1, min_t
     return wall_ms, kernel_ms, tdg.tdg_config_name(cfg)
 
 
-def time_headline(tdg, torch, w, steps, warmup, settle_s, blocks=5, block_s=0.05):
+def time_headline(tdg, torch, w, steps, warmup, settle_s, blocks=5, block_s=0.05, config=-1):
     """The headline leg: warm-up and clock settling, exactly `steps` timed
     calls (wall clock between two synchronisations, and an event pair on the
     kernel's stream), then `blocks` blocks of at least `block_s` seconds of
-    back-to-back calls for the roofline figure (median of the blocks)."""
+    back-to-back calls for the roofline figure (median of the blocks).
+    `config` >= 0 forces a tile configuration (for profiling the others)."""
     import statistics
     from workloads import TORCH_DTYPE
     a, b, c, stream = _resident(torch, w)
 
     def call():
-        tdg.gemm(a, b, layout=w.layout, out=c)
+        tdg.gemm(a, b, layout=w.layout, out=c, config=config)
     settled = warm_up(torch, call, warmup, settle_s)
     wall_ms, k_kernel_ms = timed_runs(torch, call, stream, steps)
     out = {"wall_ms": wall_ms, "k_steps_kernel_ms": k_kernel_ms, "settle_s": settled}
@@ -162,7 +163,7 @@ def time_headline(tdg, torch, w, steps, warmup, settle_s, blocks=5, block_s=0.05
         out["block_calls"] = n
     else:
         out["kernel_ms"] = k_kernel_ms
-    cfg = tdg.select_config(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
+    cfg = config if config >= 0 else tdg.select_config(a, b, layout=w.layout, out_dtype=TORCH_DTYPE[w.out_dtype])
     out["tile_config"] = tdg.tdg_config_name(cfg)
     return out
 
@@ -459,6 +460,8 @@ def main():
                     help="seconds of untimed back-to-back launches before timing (clock settling)")
     ap.add_argument("--blocks", type=int, default=5,
                     help="blocks of >= 50 ms whose median kernel time gives the roofline figure (0: the K steps)")
+    ap.add_argument("--config", default=None,
+                    help="force this tile configuration (by name) on the headline workload, for profiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -478,7 +481,14 @@ def main():
         calibrate_copy(torch)
         return
     w = WORKLOADS[args.workload]
-    h = time_headline(tdg, torch, w, args.steps, args.warmup, args.settle, blocks=args.blocks)
+    forced = -1
+    if args.config:
+        names = [tdg.tdg_config_name(i) for i in range(tdg.tdg_num_configs())]
+        if args.config not in names:
+            print("bench.py: unknown configuration %r (one of %s)" % (args.config, ", ".join(names)), file=sys.stderr)
+            sys.exit(2)
+        forced = names.index(args.config)
+    h = time_headline(tdg, torch, w, args.steps, args.warmup, args.settle, blocks=args.blocks, config=forced)
     ms, kernel_ms, cfg_name = h["wall_ms"], h["kernel_ms"], h["tile_config"]
     flops = w.flops
     value = flops / (ms * 1e-3) / 1e12
@@ -500,7 +510,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
                    "batch": w.batch, "in_dtype": w.in_dtype, "out_dtype": w.out_dtype, "accumulate": "f32",
-                   "inputs": "%s seed %d" % (w.dist, w.seed), "tile_config": cfg_name,
+                   "inputs": "%s seed %d" % (w.dist, w.seed), "tile_config": cfg_name + (" (forced)" if forced >= 0 else ""),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -131,7 +131,7 @@ __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) 
 //
 // TRANSA: false = A stored M x K (KC), true = A stored K x M (MC).
 // TRANSB: false = B stored K x N (MC), true = B stored N x K (KC).
-template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT>
+template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT, bool PP = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     constexpr int BK = 64, KS = 2, KG = 8, BNG = BN / GRAN, BMG = BM / GRAN;
     constexpr int NW = WM * WN;
@@ -158,6 +158,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // Accumulators beyond 160 registers per lane (a 4-wave 128 x 128 wave
     // tile has 256) are kept in AccVGPRs by the tied inline-assembly MFMA.
     constexpr bool ASM_ACC = (BM / WM / 16) * (BN / WN / 16) * 4 > 160;
+    static_assert(!PP || (WM == 2 && WN == 4 && STAGES == 2 && !ASM_ACC),
+                  "the ping-pong schedule: two groups of four waves (one per SIMD each), two stages");
 
     __shared__ u32x4 smem[STAGES * STAGE];
     __shared__ int sk_last;
@@ -357,7 +359,63 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 
     u32x4 af[2][RM], bf[2][RN];
 
-    if (kt_end > kt_begin) {
+    if constexpr (PP) {
+        // ---- ping-pong schedule: wave roles that alternate ----
+        // Group g = wave_m (waves 0-3 and 4-7: one wave of each group per
+        // SIMD).  Each K tile t is a memory phase -- this wave's share of the
+        // direct loads of tile t+1 into the other stage, then all of tile
+        // t's operand fragments from LDS into registers -- then a barrier,
+        // then a compute phase of nothing but the tile's 64 MFMAs, then a
+        // barrier.  Group 1 starts one phase late, so in every phase one
+        // group computes while the other loads and reads: each SIMD's MFMA
+        // pipe is fed by one wave while the other wave's memory work runs
+        // beside it (the role split of the Croqtile tutorial, chapter 4,
+        // last paragraph: a group that loads while another computes).
+        // Stage reuse: tile t sits in stage t % 2 and is read by group 0 in
+        // phase 2t and by group 1 in phase 2t+1; tile t+2 goes into that
+        // stage during phases 2t+2 (group 0's share) and 2t+3 (group 1's),
+        // after the barrier that ends phase 2t+1.  Group 0 waits for its
+        // share at the end of its compute phase 2t+3, group 1 at the end of
+        // its memory phase 2t+3, so tile t+2 is complete at the barrier
+        // before phase 2t+4, where group 0 first reads it.  The MFMAs run in
+        // the order of the other schedules, so the sums are the same bits.
+        const int g = wave_m;
+        const int nkt = kt_end - kt_begin;
+        if (nkt > 0) {
+            issue_to(kt_begin, smem);
+            wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (g == 1) __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < nkt; ++t) {
+            u32x4 *cur = smem + (t & 1) * STAGE;
+            u32x4 *nxt = smem + ((t + 1) & 1) * STAGE;
+            // memory phase
+            issue_to(kt_begin + t + 1, nxt);
+            frags_from(cur, 0, af[0], bf[0]);
+            frags_from(cur, 1, af[1], bf[1]);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (g == 1) wait_vm_lgkm0<0>();
+            else wait_vm_lgkm0<NDMA>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // compute phase
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < RM; ++i)
+#pragma unroll
+                    for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[ks][j], af[ks][i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g == 0) wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g == 0) __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    } else if (kt_end > kt_begin) {
         static_for<0, STAGES>([&](auto s) { issue_to(kt_begin + decltype(s)::value, stage_ptr(s)); });
         wait_vm_lgkm0<(STAGES - 1) * NDMA>();
         __builtin_amdgcn_s_barrier();
@@ -371,7 +429,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // of stage s_cur.  The stage is a run-time index (one loop body, no
     // per-stage copies of the code).
     int s_cur = 0;
-    if constexpr (!ASM_ACC) {
+    if constexpr (PP) {
+        // (the ping-pong loop ran above)
+    } else if constexpr (!ASM_ACC) {
         for (int kt = kt_begin; kt < kt_end; ++kt) {
             const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
             u32x4 *cur = smem + s_cur * STAGE;
