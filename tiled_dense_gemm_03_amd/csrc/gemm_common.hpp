@@ -50,7 +50,7 @@ struct F8Args {
 // tiles of BK and ST pipeline stages; KIND 0 = the register-staged kernel
 // (BK 64, two stages), VEC = vectorised loads (aligned operands) or the
 // predicated element-load path (any operands); KIND 2 = the direct-to-LDS
-// kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64); KIND 3 = its
+// kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64 or 32); KIND 3 = its
 // persistent form (one workgroup per CU walking its tiles, K > 0); KIND 4 =
 // its ping-pong form (two groups of four waves alternating a memory phase
 // and an MFMA phase; A stored M x K only).
@@ -71,7 +71,8 @@ struct F8Args {
     X(13, 2, 128, 128, 64, 2, 2, 2, true, "128x128x64_s2_w2x2_m16")          \
     X(14, 3, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16p")         \
     X(15, 2, 256, 256, 64, 2, 2, 2, true, "256x256x64_s2_w2x2_m16")          \
-    X(16, 4, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16pp")
+    X(16, 4, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16pp")        \
+    X(17, 2, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_m16")
 
 // 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
 #define TDG_F8_CONFIG_LIST(X)                                   \

@@ -21,8 +21,8 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
         hipLaunchKernelGGL((gemm_fast_kernel<BM, BN, WM, WN, BK, ST, TB, TDG_AB, CT>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 2) {
-        static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
-        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT>), dim3((unsigned)grid),
+        static_assert(BK == 64 || BK == 32, "the 16x16x32 kernel uses K tiles of 64 or 32");
+        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, false, BK>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 4) {
         static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");

@@ -124,6 +124,10 @@ __device__ __forceinline__ uint32_t records_of(int64_t elems) {
 }
 
 __device__ __forceinline__ int kx16(int r) { return (r >> 1) & 7; }                 // K-contiguous XOR
+// The same for K tiles of 32 (rows of 4 granules): the 16 rows read at once
+// by 16 lanes land on 16 distinct 16-byte bank groups.
+template <int KG>
+__device__ __forceinline__ int kxor(int r) { return KG == 8 ? (r >> 1) & 7 : (r >> 2) & 3; }
 __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }  // NN-B XOR
 
 // BM x BN workgroup tile, WM x WN waves of (BM/WM) x (BN/WN), K tiles of 64
@@ -131,9 +135,11 @@ __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) 
 //
 // TRANSA: false = A stored M x K (KC), true = A stored K x M (MC).
 // TRANSB: false = B stored K x N (MC), true = B stored N x K (KC).
-template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT, bool PP = false>
+template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT, bool PP = false,
+          int BKT = 64>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
-    constexpr int BK = 64, KS = 2, KG = 8, BNG = BN / GRAN, BMG = BM / GRAN;
+    constexpr int BK = BKT, KS = BK / 32, KG = BK / GRAN, BNG = BN / GRAN, BMG = BM / GRAN;
+    static_assert(BK == 64 || (BK == 32 && !PP), "K tiles of 64, or of 32 (one MFMA K step per stage)");
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int RM = WTM / 16, RN = WTN / 16;
@@ -146,6 +152,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     static_assert(NIA % NW == 0 && NIB % NW == 0, "whole load instructions per wave");
     constexpr int QA = NIA / NW, QB = NIB / NW, NDMA = QA + QB;
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+    static_assert(BK == 64 || STAGES >= 3, "K tiles of 32 run at least two stages ahead");
     static_assert((STAGES - 1) * NDMA < 64, "vmcnt range");
     static_assert(STAGE * 16 * STAGES <= 160 * 1024, "LDS budget");
     // An MC load instruction t covers k rows t*RP .. +RP-1 (RP = 64 granules
@@ -209,17 +216,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 
     // ---- direct-load addressing ----
     // K-contiguous operand, load q of this wave = instruction t = q*NW + wave:
-    // LDS slots 64t .. 64t+63 = rows 8t .. 8t+7, 8 granules each.  The lane's
-    // row is 8t + lane/8 and its granule g = (lane%8) ^ kx16(row); kx16 does
-    // not depend on q (NW is even), so the byte offset is a_lane + q*a_qs.
-    const int kc_row = wave * 8 + (lane >> 3);
-    const int kc_g = (lane & 7) ^ kx16(kc_row);
+    // LDS slots 64t .. 64t+63 = rows RI*t .. RI*t+RI-1 of KG granules (RI =
+    // 64 / KG: 8 rows for K tiles of 64, 16 for 32).  The lane's row is
+    // RI*t + lane/KG and its granule g = (lane%KG) ^ kxor(row); kxor does not
+    // depend on q (NW is even), so the byte offset is a_lane + q*a_qs.
+    constexpr int RI = 64 / KG;
+    const int kc_row = wave * RI + lane / KG;
+    const int kc_g = (lane % KG) ^ kxor<KG>(kc_row);
     const int kc_klim = K - kc_g * GRAN;           // granule loaded while k0 < kc_klim
     uint32_t a_lane[NVA];
     uint32_t a_qs;
     if constexpr (!TRANSA) {
         a_lane[0] = (uint32_t)((kc_row * lda + kc_g * GRAN) * 2);
-        a_qs = (uint32_t)(NW * 8 * lda * 2);
+        a_qs = (uint32_t)(NW * RI * lda * 2);
     } else {
         // MC A: as MC B below, with M for N
 #pragma unroll
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     uint32_t b_qs;
     if constexpr (TRANSB) {
         b_lane[0] = (uint32_t)((kc_row * ldb + kc_g * GRAN) * 2);
-        b_qs = (uint32_t)(NW * 8 * ldb * 2);
+        b_qs = (uint32_t)(NW * RI * ldb * 2);
     } else {
         // NN-B instruction t covers k rows RPB*t .. ; the lane's k is
         // RPB*t + lane / BNG and its column granule (lane % BNG) ^ nx16(k).
@@ -282,13 +291,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 
     // ---- fragment addresses ----
     // A (and TN-B) fragment i at K step ks: row wave_x*WT + 16 i + lane%16,
-    // granule 4 ks + lane/16; kx16 of that row is (lane>>1)&7 for every i.
+    // granule 4 ks + lane/16; kxor of that row is kxor(lane%16) for every i
+    // (rows 16 apart share the pattern).
     const int fr = lane & 15, fg = lane >> 4;
     int a_b[KS], bt_b[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        a_b[ks] = (wave_m * WTM + fr) * KG + ((4 * ks + fg) ^ ((lane >> 1) & 7));
-        bt_b[ks] = (wave_n * WTN + fr) * KG + ((4 * ks + fg) ^ ((lane >> 1) & 7));
+        a_b[ks] = (wave_m * WTM + fr) * KG + ((4 * ks + fg) ^ kxor<KG>(fr));
+        bt_b[ks] = (wave_n * WTN + fr) * KG + ((4 * ks + fg) ^ kxor<KG>(fr));
     }
     // NN-B fragment j, half h at K step ks: lane supplies the 8 bytes at k
     // row 32 ks + 8 fg + 4 h + jr, columns wave_n*WTN + 16 j + 4 q4 .. +3;
@@ -417,7 +427,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     } else if (kt_end > kt_begin) {
         static_for<0, STAGES>([&](auto s) { issue_to(kt_begin + decltype(s)::value, stage_ptr(s)); });
-        wait_vm_lgkm0<(STAGES - 1) * NDMA>();
+        // K tiles of 64: the first stage; of 32: the first two (the second
+        // one's fragments are read during the first step)
+        wait_vm_lgkm0<(BK == 32 ? STAGES - 2 : STAGES - 1) * NDMA>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         frags_from(smem, 0, af[0], bf[0]);
@@ -431,6 +443,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     int s_cur = 0;
     if constexpr (PP) {
         // (the ping-pong loop ran above)
+    } else if constexpr (BK == 32) {
+        // K tiles of 32: one MFMA K step per stage and one barrier per step.
+        // Step kt's MFMAs run interleaved with the fragment reads of step
+        // kt+1 and the direct loads of step kt+STAGES into the stage step kt
+        // occupied (its fragments were read before the previous barrier),
+        // so the loads of every step are spread over a whole step, and run
+        // STAGES steps ahead.  The wait before each barrier leaves STAGES-2
+        // steps of loads in flight: step kt+2, read during step kt+1, has
+        // landed.  Two steps per loop pass, for the two fragment buffers.
+        auto step = [&](int kt, auto xtag) {
+            constexpr int x = decltype(xtag)::value;
+            const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
+            u32x4 *cur = smem + s_cur * STAGE;
+            u32x4 *nxt = smem + s_nxt * STAGE;
+            constexpr int NSUB = NDMA;
+            static_for<0, NSUB>([&](auto sub) {
+                constexpr int s0 = decltype(sub)::value;
+                static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
+                    constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                    acc[i][j] = mfma_16x16x32<AB>(bf[x][j], af[x][i], acc[i][j]);
+                });
+                static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>(
+                    [&](auto d) { frag_op(d, nxt, 0, af[1 - x], bf[1 - x]); });
+                dma_op(sub, kt + STAGES, cur);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vm_lgkm0<(STAGES - 2) * NDMA>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            s_cur = s_nxt;
+        };
+        for (int kt = kt_begin; kt < kt_end; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            if (kt + 1 < kt_end) step(kt + 1, std::integral_constant<int, 1>{});
+        }
     } else if constexpr (!ASM_ACC) {
         for (int kt = kt_begin; kt < kt_end; ++kt) {
             const int s_nxt = (s_cur + 1 == STAGES) ? 0 : s_cur + 1;
