@@ -124,14 +124,22 @@ tdg_status tdg_gemm_ex(int transb, int64_t M, int64_t N, int64_t K,
  * program and names the alternative, splitting K over programs, together
  * with its cost: a merge step.  tdg_gemm_ws is tdg_gemm_ex with the
  * library's own choice of configuration plus a caller-owned workspace that
- * enables a split-K schedule: when the output tiles do not fill whole rounds
- * of the device's compute units (e.g. 320 tiles on 256 CUs), or there are
- * few tiles with a long K, the tiles of the last partial round are each cut
- * into K slices run by separate workgroups; each slice writes an fp32
- * partial tile into the workspace and the last slice to finish adds them in
- * slice order and writes C.  The result is the same sum with another
- * rounding order (bitwise equal for exactly representable sums), and it is
- * deterministic: the same call on the same device gives the same bits.
+ * enables split-K schedules, in which some output tiles are each cut into K
+ * slices run by separate workgroups; each slice writes an fp32 partial tile
+ * into the workspace and the last slice to finish adds them in slice order
+ * and writes C:
+ *   - few tiles with a long K (fewer 128 x 128 tiles than compute units):
+ *     every tile is cut into slices;
+ *   - a single problem whose 256 x 256 tiles leave a partial last round
+ *     (e.g. 289 tiles on 256 CUs): one launch in which the tiles of whole
+ *     rounds are whole work items and the tiles of the partial round are
+ *     cut into slices, when no band of whole rounds can be cut off or the
+ *     rest of such a cut would fill fewer than half of the compute units
+ *     (otherwise the band and the rest run as two launches, without a
+ *     workspace).
+ * The result is the same sum with another rounding order (bitwise equal for
+ * exactly representable sums), and it is deterministic: the same call on the
+ * same device gives the same bits.
  *
  * workspace: device memory, 256-byte aligned, at least
  *   tdg_gemm_workspace_size(...) bytes for these sizes, zero-filled before its

@@ -154,7 +154,12 @@ def test_split_k_workspace_plan(tdg):
     ws = lambda transb, M, N, K, batch=1: tdg.tdg_gemm_workspace_size(transb, M, N, K, batch, 256)
     assert ws(0, 8192, 8192, 8192) == 0                        # 1024 tiles of 256 x 256
     assert ws(1, 2048, 2048, 128, 32) == 0                     # 2048 tiles
-    assert ws(0, 4095, 5000, 3000) == 0                        # 320 tiles: cut, not split
+    # 320 tiles of 256 x 256: 256 whole tiles, the other 64 in 4 K slices of 11-12 K tiles
+    assert ws(0, 4095, 5000, 3000) == 64 * 4 * 256 * 256 * 4 + 1024
+    assert ws(1, 5000, 4095, 3000) == 64 * 4 * 256 * 256 * 4 + 1024
+    assert ws(0, 4352, 4096, 1024) == 16 * 2 * 256 * 256 * 4 + 1024   # 272 tiles: 16 left over, 2 slices of 8
+    assert ws(0, 4352, 4096, 256) == 0                         # 4 K tiles: too short to split (and persistent)
+    assert ws(0, 4096, 4096, 4096, 2) == 0                     # batched: no partial-round split
     assert ws(0, 2048, 2048, 8192) == 0                        # 256 tiles of 128 x 128
     assert ws(0, 1024, 1024, 16384) == 64 * 4 * tile + 1024    # 64 tiles, 4 slices of 64 K tiles
     assert ws(0, 1024, 1024, 1024) == 0                        # 16 K tiles: too short to split
@@ -166,15 +171,16 @@ def test_split_k_workspace_plan(tdg):
 
 
 def test_split_k_workspace_bound(tdg):
-    """The bound serves every call: at most one 128 x 128 fp32 partial per CU
-    after the counter block, and at least every size the plan asks for."""
-    tile = 128 * 128 * 4
+    """The bound serves every call: at most one 256 x 256 fp32 partial per CU
+    after the counter block, and at least every size the plans ask for."""
+    tile = 256 * 256 * 4
     for cus in (64, 80, 256, 304):
         bound = tdg.tdg_gemm_workspace_bound(cus)
         assert bound == cus * tile + (cus * 4 + 255) // 256 * 256
         for transb in (0, 1):
             for M, N, K in ((1024, 1024, 16384), (300, 520, 16384), (512, 256, 16384), (128, 128, 1 << 20),
-                            (130, 1000, 65536), (4000, 100, 100000), (1, 1, 1 << 24)):
+                            (130, 1000, 65536), (4000, 100, 100000), (1, 1, 1 << 24), (4095, 5000, 3000),
+                            (4352, 4096, 1 << 20), (8448, 8192, 4096)):
                 for batch in (1, 2, 3):
                     assert tdg.tdg_gemm_workspace_size(transb, M, N, K, batch, cus) <= bound
 

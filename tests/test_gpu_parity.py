@@ -372,6 +372,43 @@ def test_partial_round_cut_exact(tdg, layout, M, N, K):
     check_exact(cf[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f32", "cut fp32 %dx%dx%d" % (M, N, K))
 
 
+# A partial last round of 256 x 256 tiles served in one launch: whole tiles,
+# then the left-over tiles cut into K slices merged by the last slice to
+# finish (the library picks it when no band of whole rounds exists, or when
+# the 128 x 128 rest of the two-launch cut would fill fewer than half of the
+# CUs).  (M, N, K): 17 x 17 tiles with no band; a band of 16 tile columns
+# with a rest of 64 small tiles; the same cut in rows.
+ROUND_SPLIT_SHAPES = [(4352, 4352, 1024), (4096, 4352, 2048), (4352, 4096, 2048)]
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("M,N,K", ROUND_SPLIT_SHAPES)
+def test_round_split_exact_and_deterministic(tdg, layout, M, N, K):
+    announce("round split", layout, M, N, K)
+    assert tdg.tdg_gemm_workspace_size(1 if layout == "tn" else 0, M, N, K, 1, 0) > 0, "should plan a K split"
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M + N + K + 7)
+    ad, bd = a.cuda(), b.cuda()
+    c1 = tdg.gemm(ad, bd, layout=layout, out_dtype=torch.float32)
+    c2 = tdg.gemm(ad, bd, layout=layout, out_dtype=torch.float32)
+    c3 = tdg.gemm(ad, bd, layout=layout, out_dtype=torch.float32, split_k=False)   # no workspace: the cut
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2), "the one-launch schedule is not deterministic"
+    rows = sample_rows(M)
+    ref = ref_gemm(a, b, "bf16", layout, rows=rows)
+    check_exact(c1.cpu()[rows], ref, "f32", "round split %s %dx%dx%d" % (layout, M, N, K))
+    check_exact(c3.cpu()[rows], ref, "f32", "without workspace %s %dx%dx%d" % (layout, M, N, K))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_round_split_random_tolerance(tdg, layout):
+    M, N, K = 4352, 4352, 2048
+    announce("round split random", layout, M, N, K)
+    a, b = make_inputs(M, N, K, layout, "f16", "normal_k", seed=88)
+    c = gpu_gemm(tdg, a, b, layout, "f16")
+    rows = sample_rows(M)
+    check_tol(c[rows], ref_gemm(a, b, "f16", layout, rows=rows), "f16", K, "round split random")
+
+
 @pytest.mark.parametrize("layout", ["nn", "tn"])
 def test_output_ownership_map(tdg, layout):
     """Every output element is written exactly once, by the lane that owns

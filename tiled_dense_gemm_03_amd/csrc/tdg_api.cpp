@@ -144,9 +144,8 @@ int config_by_name(const char *name) {
 // tiles than that would leave most of the chip idle; each tile is cut
 // instead into `split` K slices (at most cus / tiles, each at least
 // kMinSliceTiles K tiles), run by separate workgroups and merged by the last
-// slice to finish.  (The kernel also takes whole tiles before the split ones;
-// for a partial last round the merge traffic costs more than it saves, and
-// the cut into 256 x 256 and 128 x 128 parts below serves that case.)
+// slice to finish.  The kernel also takes whole tiles before the split
+// ones, which serves a partial last round (plan_round_split below).
 constexpr int64_t kMinSliceTiles = 16;
 
 struct SplitPlan {
@@ -169,6 +168,30 @@ SplitPlan plan_split(int64_t tiles, int64_t nk, int64_t cus) {
     return pl;
 }
 
+// A partial last round in one launch (stream-K style: whole tiles, then the
+// tiles of the partial round cut into K slices that fill the chip): more
+// 256 x 256 tiles than `cus` but not a whole number of rounds, e.g. 320
+// tiles on 256 CUs.  The tiles of whole rounds are whole-tile work items;
+// the `rem` tiles left over are each cut into at most cus / rem K slices of
+// at least kMinRoundSliceTiles K tiles, merged by the last slice to finish.
+// Workgroups that finish their whole tile early start on the slices, so the
+// last round is spread over every CU instead of running on rem of them.
+constexpr int64_t kMinRoundSliceTiles = 8;
+
+SplitPlan plan_round_split(int64_t tiles, int64_t nk, int64_t cus) {
+    SplitPlan pl{tiles, 0, 1};
+    if (cus <= 0 || tiles <= cus) return pl;
+    const int64_t rem = tiles % cus;
+    if (rem == 0) return pl;
+    int64_t sp = cus / rem;
+    if (sp > nk / kMinRoundSliceTiles) sp = nk / kMinRoundSliceTiles;
+    if (sp < 2) return pl;
+    pl.dp_tiles = tiles - rem;
+    pl.sk_tiles = rem;
+    pl.split = (int)sp;
+    return pl;
+}
+
 // Workspace layout: one int counter per possible split tile (fewer than
 // `cus` of them) at the start, padded to 256 bytes, then the fp32 partial
 // tiles (split x sk_tiles of them).  The counters sit at the same place
@@ -181,11 +204,14 @@ size_t split_ws_bytes(const Config &cf, const SplitPlan &pl, int64_t cus) {
 }
 
 // The largest workspace any call needs on a device with `cus` compute units.
-// Only the automatic choice splits K, and only for problems with fewer tiles
-// than CUs, which it serves with 128 x 128 tiles (256 x 256 tiles are chosen
-// only for at least one tile per CU); plan_split gives at most `cus` slices
-// in all (rem * floor(cus / rem) <= cus).
-size_t split_ws_bound(int64_t cus) { return split_flag_bytes(cus) + (size_t)cus * 128 * 128 * 4; }
+// Only the automatic choice splits K: problems with fewer tiles than CUs on
+// 128 x 128 tiles (256 x 256 tiles are chosen only for at least one tile
+// per CU), and partial last rounds of 256 x 256 tiles; each plan gives at
+// most `cus` slices in all (rem * floor(cus / rem) <= cus).  The first kind
+// fits in split_ws_bound_small; a call whose workspace cannot hold the
+// second serves the partial round another way (the cut in run()).
+size_t split_ws_bound_small(int64_t cus) { return split_flag_bytes(cus) + (size_t)cus * 128 * 128 * 4; }
+size_t split_ws_bound(int64_t cus) { return split_flag_bytes(cus) + (size_t)cus * 256 * 256 * 4; }
 
 // Whether a split schedule is worth taking for a problem below one round of
 // 256 x 256 tiles: it must give at least half the chip a work item.
@@ -273,7 +299,8 @@ tdg_status validate(int transa, int transb, int transc, int64_t M, int64_t N, in
 tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                   int64_t sA,
                   const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc, int64_t sC, int64_t batch,
-                  tdg_dtype ab_type, tdg_dtype c_type, void *stream, void *ws, size_t ws_bytes, int cus) {
+                  tdg_dtype ab_type, tdg_dtype c_type, void *stream, void *ws, size_t ws_bytes, int cus,
+                  const SplitPlan *plan = nullptr) {
     const Config &cf = kConfigs[config];
     GemmArgs a;
     a.A = static_cast<const uint16_t *>(A);
@@ -312,7 +339,9 @@ tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int6
         return TDG_SUCCESS;
     }
     SplitPlan pl{tiles, 0, 1};
-    if (cf.kind == 2 && ws != nullptr) {
+    if (plan != nullptr) {
+        pl = *plan;
+    } else if (cf.kind == 2 && ws != nullptr) {
         pl = plan_split(tiles, cdiv(K, cf.bk), cus);
         if (!split_pays(pl, cus)) pl = SplitPlan{tiles, 0, 1};
     }
@@ -466,8 +495,28 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
     const Config &cf = kConfigs[config];
 
     // Automatic choice on a single problem with a partial last round of
-    // 256 x 256 tiles: whole rounds on one band of C, 128 x 128 tiles on the
-    // rest (two launches on the stream, disjoint parts of C).
+    // 256 x 256 tiles: whole rounds on one band of C and 128 x 128 tiles on
+    // the rest (two launches on the stream, disjoint parts of C), or one
+    // launch whose last round is cut into K slices (plan_round_split), when
+    // the workspace holds their partial tiles and either no band of whole
+    // rounds exists or the 128 x 128 rest would keep fewer than half of the
+    // CUs busy.  Measured on MI355X (one launch / two launches): 0.71 and
+    // 0.85 with no band (17 x 17 tiles, K 16384 and 4096), 0.85 with a rest
+    // of 64 small tiles (K 32768), 0.98 with a rest of 128, 1.03 and 1.13
+    // with rests of 128 and 256 (4095 x 5000 x 3000): the merge of 256 x 256
+    // partial tiles costs more than a well-filled rest round.
+    if (automatic && !tuned && cf.kind == 2 && batch == 1 && ws != nullptr) {
+        const SplitPlan rp = plan_round_split(cdiv(M, cf.bm) * cdiv(N, cf.bn), cdiv(K, cf.bk), cus);
+        if (rp.split >= 2 && split_ws_bytes(cf, rp, cus) <= ws_bytes) {
+            bool cols = true;
+            const int64_t cut = plan_retile(M, N, cus, &cols);
+            const int64_t rest = cut == 0 ? 0
+                                 : (cols ? cdiv(M, 128) * cdiv(N - cut, 128) : cdiv(M - cut, 128) * cdiv(N, 128));
+            if (cut == 0 || rest * 2 < cus)
+                return launch(config, transa, transb, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, ab_type,
+                              c_type, stream, ws, ws_bytes, cus, &rp);
+        }
+    }
     if (automatic && !tuned && cf.kind >= 2 && batch == 1) {
         const int small = config_by_name("128x128x64_s4_w2x4_m16");
         bool cols = true;
@@ -653,10 +702,10 @@ tdg_status tdg_gemm_noalloc(int transa, int transb, int transc, int64_t M, int64
     int cus = 0, dev = 0;
     st = check_device(&cus, &dev);
     if (st != TDG_SUCCESS) return st;
-    if (split_ws_bound(cus) > kScratchBytes)
+    if (split_ws_bound_small(cus) > kScratchBytes)
         return fail(TDG_INVALID_VALUE,
                     "the split-K schedule of a %d-CU device may need %zu bytes, more than the %zu-byte scratch array",
-                    cus, split_ws_bound(cus), kScratchBytes);
+                    cus, split_ws_bound_small(cus), kScratchBytes);
     void *ws = nullptr;
     st = scratch_of(dev, &ws);
     if (st != TDG_SUCCESS) return st;
@@ -732,6 +781,11 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
     const tdg::Config &cf = tdg::kConfigs[id];
     if (cf.kind != 2) return 0;
     const int64_t tiles = tdg::cdiv(M, cf.bm) * tdg::cdiv(N, cf.bn) * batch;
+    if (batch == 1 && tiles > cus) {
+        // (an upper bound: run() may serve the problem with the cut instead)
+        const tdg::SplitPlan rp = tdg::plan_round_split(tiles, tdg::cdiv(K, cf.bk), cus);
+        return rp.split >= 2 ? tdg::split_ws_bytes(cf, rp, cus) : 0;
+    }
     const tdg::SplitPlan pl = tdg::plan_split(tiles, tdg::cdiv(K, cf.bk), cus);
     if (!tdg::split_pays(pl, cus)) return 0;
     return tdg::split_ws_bytes(cf, pl, cus);
