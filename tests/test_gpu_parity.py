@@ -548,14 +548,16 @@ def test_autotune_transposed_operands(tdg):
 # ---------------------------------------------------------------------------
 
 # The library's own choice of the persistent kernel: two or more rounds of
-# 256 x 256 tiles with K <= 512, in both layouts and with 16-bit and fp32
-# output (the automatic path, not a forced configuration).
+# 256 x 256 tiles with K <= 512 (16-bit output) or K <= 128 (fp32 output), in
+# both layouts (the automatic path, not a forced configuration).
 @pytest.mark.parametrize("layout,M,N,K,batch,in_dtype,out_dtype", [("nn", 4096, 4096, 320, 2, "bf16", "bf16"),
-                                                                   ("tn", 6100, 5400, 192, 0, "f16", "f32"),
-                                                                   ("nn", 2048, 2048, 512, 8, "f16", "f32"),
+                                                                   ("tn", 6100, 5400, 120, 0, "f16", "f32"),
+                                                                   ("tn", 6100, 5400, 192, 0, "f16", "f16"),
+                                                                   ("nn", 2048, 2048, 512, 8, "f16", "f16"),
+                                                                   ("nn", 2048, 2048, 128, 8, "bf16", "f32"),
                                                                    # 32 x 17 tiles: cut into 32 x 16 on the
                                                                    # persistent kernel and a 128 x 128 rest
-                                                                   ("nn", 8192, 4352, 256, 0, "bf16", "f32")])
+                                                                   ("nn", 8192, 4352, 256, 0, "bf16", "bf16")])
 def test_automatic_persistent_choice_exact(tdg, layout, M, N, K, batch, in_dtype, out_dtype):
     announce("auto persistent", layout, M, N, K, batch, in_dtype, out_dtype)
     a, b = make_inputs(M, N, K, layout, in_dtype, "ints", seed=M + K + batch, batch=batch)
