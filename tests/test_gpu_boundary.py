@@ -206,3 +206,40 @@ def test_degenerate_sizes(lib):
     assert st == 0
     torch.cuda.synchronize()
     assert bool((buf2.cpu() == SENTINEL).all())
+
+
+# Edge tiles of the 16 x 16 x 32 kernels' epilogue: a right-edge tile cut by
+# N (whole 16-byte chunks, a chunk cut inside, chunks past N) and 16-bit rows
+# that start 2 bytes past a 4-byte boundary (odd ldc: every other row), each
+# configuration forced, integer inputs, C inside a guard-banded frame.
+# (layout, M, N, K, ldc, out_dtype)
+EDGE_STORE_CASES = [("nn", 300, 520, 128, 521, "f16"), ("tn", 260, 389, 64, 389, "bf16"),
+                    ("tn", 300, 520, 128, 523, "f32"), ("nn", 129, 264, 64, 265, "bf16"),
+                    ("tn", 257, 1000, 96, 1003, "f16")]
+
+
+def _m16_configs(lib):
+    out = []
+    for i in range(lib.tdg_num_configs()):
+        name = lib.tdg_config_name(i).decode()
+        if "_m16" in name and not name.endswith("_m16p"):
+            out.append((i, name))
+    return out
+
+
+@pytest.mark.parametrize("layout,M,N,K,ldc,out_dtype", EDGE_STORE_CASES)
+def test_edge_tile_stores_every_m16_config(lib, layout, M, N, K, ldc, out_dtype):
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M + N + K + ldc)
+    ref = ref_gemm(a, b, "bf16", layout)
+    ad, bd = a.cuda(), b.cuda()
+    ldb = N if layout == "nn" else K
+    for cfg, name in _m16_configs(lib):
+        announce("edge stores", name, layout, M, N, K, ldc, out_dtype)
+        buf, off, _ = framed_c(M, N, ldc, out_dtype)
+        es = buf.element_size()
+        st = lib.tdg_gemm_ex(1 if layout == "tn" else 0, M, N, K, ad.data_ptr(), K, 0, bd.data_ptr(), ldb, 0,
+                             buf.data_ptr() + off * es, ldc, 0, 1, CODE["bf16"], CODE[out_dtype], cfg, stream_ptr())
+        assert st == 0, (name, lib.tdg_last_error().decode())
+        torch.cuda.synchronize()
+        check_frame(buf, off, M, N, ldc)
+        check_exact(view_c(buf, off, M, N, ldc).cpu(), ref, out_dtype, "edge stores %s %s" % (name, layout))

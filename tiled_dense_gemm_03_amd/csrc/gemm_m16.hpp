@@ -617,133 +617,140 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
 
     // ---- epilogue: fp32 -> output type, store mask of the primer's s5 ----
     // Lane l holds C[m][n] for m = 16 i + l % 16, n = 16 j + 4 (l / 16) + r.
-    // Interior tiles go through LDS a band of whole tile rows at a time (see
-    // below) and are stored as complete rows.  Where the tile passes N or C
-    // is not 4-byte aligned, one 16-row block of the wave's sub-tile at a
-    // time goes through the wave's own LDS region in fp32; each lane reads
-    // back 4 consecutive values of a row, converts them (round to nearest
-    // even) and stores them element by element.  Rows past M are never
-    // stored.
+    // The tile goes through LDS a band of whole tile rows at a time: in pass
+    // p, the waves that hold rows p*PR .. p*PR + PR - 1 write them, converted
+    // to the output type (round to nearest even), into LDS (row stride
+    // BN*ES + 16 bytes); after a barrier every wave reads back whole tile
+    // rows (16 bytes per lane, LPR lanes per row) and stores them, so each
+    // store instruction writes one or more complete BN-wide rows of C.  A
+    // lane whose 16 bytes lie inside N on a 4-byte aligned row stores them
+    // with one 16-byte store; rows past M are never stored.  Only on an edge
+    // tile (it passes N, or C's rows are not all 4-byte aligned) does a
+    // second step store what the 16-byte stores left out: a chunk cut by N
+    // element by element, a whole 16-bit chunk on a row that starts 2 bytes
+    // past a 4-byte boundary as one element, three element pairs and one
+    // element (all naturally aligned).  Chunks past N are never stored.
     constexpr int ES = (CT == OUT_F32) ? 4 : 2;
-    constexpr int ROWB = WTN * 4 + 16;             // staged row: fp32, padded by 16 bytes
-    constexpr int CPR = WTN / 4;                   // 4-column chunks per row
-    constexpr int RPI = 64 / CPR;                  // rows per read-back instruction
-    static_assert(RPI * CPR == 64 && 16 % RPI == 0, "row chunks must tile a wave");
-    static_assert(NW * 16 * ROWB <= STAGES * STAGE * 16, "epilogue staging fits in LDS");
+    constexpr int CE = 16 / ES;                    // elements per 16-byte chunk
     const char *Cbase = (const char *)p.C + ((int64_t)batch * p.sC + (int64_t)m0 * p.ldc + n0) * ES;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase);
-    const bool vec_store = (n0 + BN <= N) && (((uintptr_t)p.C | (uintptr_t)(p.ldc * ES) | (uintptr_t)(p.sC * ES)) & 3) == 0;
+    const int valid_n = N - n0;                    // columns of C from this tile's first one
+    const bool rows_al4 = (((uintptr_t)Cbase | (uintptr_t)(p.ldc * ES)) & 3) == 0;
+    const bool edge = valid_n < BN || !rows_al4;   // uniform over the workgroup
     __builtin_amdgcn_s_barrier();                  // every wave is done with the stages
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    char *const region = reinterpret_cast<char *>(smem) + wave * 16 * ROWB;
     const int wrow = lane & 15, wcol = 4 * (lane >> 4);
-    constexpr int NT = 16 / RPI;                   // read-back instructions per 16-row block
-    if (vec_store) {
-        // Interior tile: whole rows of the workgroup's tile at a time.  In
-        // pass p, the waves that hold rows p*PR .. p*PR + PR - 1 write them,
-        // converted to the output type, into LDS (row stride BN*ES + 16
-        // bytes); after a barrier every wave reads back whole tile rows
-        // (16 bytes per lane, LPR lanes per row) and stores them, so each
-        // store instruction writes one or more complete BN-wide rows of C.
-        constexpr int RS = BN * ES + 16;
-        constexpr int BUDGET = STAGES * STAGE * 16;
-        constexpr int PR = (WTM * RS <= BUDGET) ? WTM : (WTM / 2 * RS <= BUDGET) ? WTM / 2 : WTM / 4;
-        static_assert(PR % 16 == 0 && WTM % PR == 0 && PR * RS <= BUDGET, "epilogue pass fits in LDS");
-        constexpr int LPR = BN * ES / 16;                 // lanes per row
-        static_assert(64 % LPR == 0, "whole rows per store instruction");
-        constexpr int RPS = 64 / LPR;                     // rows per store instruction
-        static_assert(PR % (NW * RPS) == 0, "rows spread evenly over the waves");
-        constexpr int NST = PR / (NW * RPS);              // store instructions per wave and pass
-        char *const rows = reinterpret_cast<char *>(smem);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int RS = BN * ES + 16;
+    constexpr int BUDGET = STAGES * STAGE * 16;
+    constexpr int PR = (WTM * RS <= BUDGET) ? WTM : (WTM / 2 * RS <= BUDGET) ? WTM / 2 : WTM / 4;
+    static_assert(PR % 16 == 0 && WTM % PR == 0 && PR * RS <= BUDGET, "epilogue pass fits in LDS");
+    constexpr int LPR = BN * ES / 16;                 // lanes per row
+    static_assert(64 % LPR == 0, "whole rows per store instruction");
+    constexpr int RPS = 64 / LPR;                     // rows per store instruction
+    static_assert(PR % (NW * RPS) == 0, "rows spread evenly over the waves");
+    constexpr int NST = PR / (NW * RPS);              // store instructions per wave and pass
+    char *const rows = reinterpret_cast<char *>(smem);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int cc = (lane % LPR) * CE;                 // first column of the lane's chunk
+    const bool full = cc + CE <= valid_n;
 #pragma unroll
-        for (int pass = 0; pass < BM / PR; ++pass) {
-            constexpr int BPP = PR / 16;                  // 16-row blocks per pass
-            if (wave_m == pass * PR / WTM) {
-                const int i0 = (pass * PR % WTM) / 16;
+    for (int pass = 0; pass < BM / PR; ++pass) {
+        constexpr int BPP = PR / 16;                  // 16-row blocks per pass
+        if (wave_m == pass * PR / WTM) {
+            const int i0 = (pass * PR % WTM) / 16;
 #pragma unroll
-                for (int ib = 0; ib < BPP; ++ib) {
+            for (int ib = 0; ib < BPP; ++ib) {
 #pragma unroll
-                    for (int j = 0; j < RN; ++j) {
-                        // (i0 + ib) is uniform; select the block without
-                        // dynamic indexing of the accumulator array
-                        f32x4 v = acc[0][j];
+                for (int j = 0; j < RN; ++j) {
+                    // (i0 + ib) is uniform; select the block without
+                    // dynamic indexing of the accumulator array
+                    f32x4 v = acc[0][j];
 #pragma unroll
-                        for (int i = 1; i < RM; ++i) if (i == i0 + ib) v = acc[i][j];
-                        char *dst = rows + (ib * 16 + wrow) * RS + (wave_n * WTN + 16 * j + wcol) * ES;
-                        if constexpr (CT == OUT_F32) {
-                            *reinterpret_cast<f32x4 *>(dst) = v;
+                    for (int i = 1; i < RM; ++i) if (i == i0 + ib) v = acc[i][j];
+                    char *dst = rows + (ib * 16 + wrow) * RS + (wave_n * WTN + 16 * j + wcol) * ES;
+                    if constexpr (CT == OUT_F32) {
+                        *reinterpret_cast<f32x4 *>(dst) = v;
+                    } else {
+                        u32x2 w;
+                        if constexpr (CT == OUT_F16) {
+                            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+                            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
                         } else {
-                            u32x2 w;
-                            if constexpr (CT == OUT_F16) {
-                                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
-                                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
-                            } else {
-                                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-                                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+                            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+                            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+                        }
+                        *reinterpret_cast<u32x2 *>(dst) = w;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        u32x4 w[NST];
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const int r = (wave * NST + t) * RPS + lane / LPR;
+            w[t] = *reinterpret_cast<const u32x4 *>(rows + r * RS + (lane % LPR) * 16);
+        }
+#pragma unroll
+        for (int t = 0; t < NST; ++t) {
+            const int cm = pass * PR + (wave * NST + t) * RPS + lane / LPR;
+            const bool al4 = (((uintptr_t)Cbase + (uintptr_t)((int64_t)cm * p.ldc * ES)) & 3) == 0;
+            const uint32_t off = (m0 + cm < M && full && al4) ? (uint32_t)(cm * p.ldc * ES + cc * ES) : OOB_OFFSET;
+            __builtin_amdgcn_raw_buffer_store_b128(w[t], rc, off, 0, STORE_NT);
+        }
+        store_data_read_all(w);
+        if (edge) {
+#pragma unroll
+            for (int t = 0; t < NST; ++t) {
+                const int cm = pass * PR + (wave * NST + t) * RPS + lane / LPR;
+                const bool al4 = (((uintptr_t)Cbase + (uintptr_t)((int64_t)cm * p.ldc * ES)) & 3) == 0;
+                if (m0 + cm < M && cc < valid_n && !(full && al4)) {
+                    const uint32_t row_off = (uint32_t)(cm * p.ldc + cc) * ES;
+                    if constexpr (ES == 2) {
+                        if (full) {
+                            // 16-bit row starting 2 bytes past a 4-byte
+                            // boundary: e0, (e1 e2), (e3 e4), (e5 e6), e7
+                            const uint16_t e0 = (uint16_t)w[t][0], e7 = (uint16_t)(w[t][3] >> 16);
+                            const uint32_t p0 = (w[t][0] >> 16) | (w[t][1] << 16);
+                            const uint32_t p1 = (w[t][1] >> 16) | (w[t][2] << 16);
+                            const uint32_t p2 = (w[t][2] >> 16) | (w[t][3] << 16);
+                            __builtin_amdgcn_raw_buffer_store_b16(e0, rc, row_off, 0, STORE_NT);
+                            __builtin_amdgcn_raw_buffer_store_b32(p0, rc, row_off + 2, 0, STORE_NT);
+                            __builtin_amdgcn_raw_buffer_store_b32(p1, rc, row_off + 6, 0, STORE_NT);
+                            __builtin_amdgcn_raw_buffer_store_b32(p2, rc, row_off + 10, 0, STORE_NT);
+                            __builtin_amdgcn_raw_buffer_store_b16(e7, rc, row_off + 14, 0, STORE_NT);
+                            store_data_read(e0);
+                            store_data_read(p0);
+                            store_data_read(p1);
+                            store_data_read(p2);
+                            store_data_read(e7);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < CE; ++e) {
+                                const uint16_t x = (uint16_t)(w[t][e / 2] >> (16 * (e % 2)));
+                                const uint32_t o = cc + e < valid_n ? row_off + 2 * e : OOB_OFFSET;
+                                __builtin_amdgcn_raw_buffer_store_b16(x, rc, o, 0, STORE_NT);
+                                store_data_read(x);
                             }
-                            *reinterpret_cast<u32x2 *>(dst) = w;
+                        }
+                    } else {
+                        // fp32: rows are 4-byte aligned, so only a chunk cut by N gets here
+#pragma unroll
+                        for (int e = 0; e < CE; ++e) {
+                            const uint32_t x = w[t][e];
+                            const uint32_t o = cc + e < valid_n ? row_off + 4 * e : OOB_OFFSET;
+                            __builtin_amdgcn_raw_buffer_store_b32(x, rc, o, 0, STORE_NT);
+                            store_data_read(x);
                         }
                     }
                 }
             }
-            __syncthreads();
-            u32x4 w[NST];
-#pragma unroll
-            for (int t = 0; t < NST; ++t) {
-                const int r = (wave * NST + t) * RPS + lane / LPR;
-                w[t] = *reinterpret_cast<const u32x4 *>(rows + r * RS + (lane % LPR) * 16);
-            }
-#pragma unroll
-            for (int t = 0; t < NST; ++t) {
-                const int r = (wave * NST + t) * RPS + lane / LPR;
-                const int cm = pass * PR + r;
-                const uint32_t off = m0 + cm < M ? (uint32_t)(cm * p.ldc * ES + (lane % LPR) * 16) : OOB_OFFSET;
-                __builtin_amdgcn_raw_buffer_store_b128(w[t], rc, off, 0, STORE_NT);
-            }
-            store_data_read_all(w);
-            if (pass + 1 < BM / PR) __syncthreads();      // the rows are rewritten by the next pass
         }
-        return;
-    }
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-#pragma unroll
-        for (int j = 0; j < RN; ++j) {
-            *reinterpret_cast<f32x4 *>(region + wrow * ROWB + (16 * j + wcol) * 4) = acc[i][j];
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int row = t * RPI + lane / CPR, chunk = lane % CPR;
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(region + row * ROWB + chunk * 16);
-            const int cm = wave_m * WTM + i * 16 + row;
-            const int cn = wave_n * WTN + chunk * 4;
-            const bool row_ok = m0 + cm < M;
-            // element by element: the tile passes N, or C is not 4-byte aligned
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t off = (row_ok && n0 + cn + r < N) ? (uint32_t)(cm * p.ldc + cn + r) * ES : OOB_OFFSET;
-                if constexpr (CT == OUT_F32) {
-                    // (the words of the whole vector: hipcc's bit cast of a
-                    // single vector element reads element 0 whatever the index)
-                    const uint32_t x = __builtin_bit_cast(u32x4, v)[r];
-                    __builtin_amdgcn_raw_buffer_store_b32(x, rc, off, 0, STORE_NT);
-                    store_data_read(x);
-                } else if constexpr (CT == OUT_F16) {
-                    const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)v[r]);
-                    __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
-                    store_data_read(x);
-                } else {
-                    const uint16_t x = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-                    __builtin_amdgcn_raw_buffer_store_b16(x, rc, off, 0, STORE_NT);
-                    store_data_read(x);
-                }
-            }
-        }
+        if (pass + 1 < BM / PR) __syncthreads();      // the rows are rewritten by the next pass
     }
 }
 
