@@ -123,11 +123,12 @@ def test_config_selection(tdg):
     assert sel(1, 4096, 4096, 4096) == "256x256x64_s2_w2x4_m16"
     assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16"
     # the persistent kernel: several rounds of 256 x 256 tiles and K <= 512
-    # (K <= 128 for fp32 output)
+    # (fp32 output: batches only)
     assert sel(1, 2048, 2048, 128, batch=32) == "256x256x64_s2_w2x4_m16p"
     assert sel(1, 2048, 2048, 128, batch=32, c_type=2) == "256x256x64_s2_w2x4_m16p"
-    assert sel(1, 2048, 2048, 136, batch=32, c_type=2) == "256x256x64_s2_w2x4_m16"
-    assert sel(0, 4096, 4096, 512, batch=4, c_type=2) == "256x256x64_s2_w2x4_m16"
+    assert sel(0, 4096, 4096, 512, batch=4, c_type=2) == "256x256x64_s2_w2x4_m16p"
+    assert sel(1, 8192, 8192, 128, c_type=2) == "256x256x64_s2_w2x4_m16"       # fp32, single problem
+    assert sel(1, 8192, 8192, 128) == "256x256x64_s2_w2x4_m16p"
     assert sel(0, 4096, 4096, 512, batch=4) == "256x256x64_s2_w2x4_m16p"
     assert sel(0, 4096, 4096, 520, batch=4) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 4096, 4096, 256) == "256x256x64_s2_w2x4_m16"          # a single round

@@ -331,13 +331,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16p_kernel(GemmArgs p) {
                         const int Rr = (wave * NT + t) * RPI + lane / CPR32, c = lane % CPR32;
                         w[t] = *reinterpret_cast<const u32x4 *>(stg + Rr * RB + ((c ^ (Rr & 15)) * 16));
                     }
+                    static_assert(RPI == 1, "one tile row per store instruction");
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        const int Rr = (wave * NT + t) * RPI + lane / CPR32, c = lane % CPR32;
+                        // the row is uniform over the wave: its offset goes in
+                        // the scalar operand and the row test is a branch, so
+                        // only the lane's 16-byte column offset is per lane
+                        // (per-lane row offsets hoisted out of the tile walk
+                        // would not fit in the register file)
+                        const int Rr = wave * NT + t;
                         const int row = (Rr / 16) * WTM + 16 * i + Rr % 16;     // row of the tile
-                        const uint32_t off =
-                            m0 + row < M ? (uint32_t)(row * p.ldc + c * 4) * ES : OOB_OFFSET;
-                        __builtin_amdgcn_raw_buffer_store_b128(w[t], rc_tile, off, 0, STORE_NT);
+                        if (m0 + row < M)
+                            __builtin_amdgcn_raw_buffer_store_b128(w[t], rc_tile, (uint32_t)lane * 16u,
+                                                                   (int)((int64_t)row * p.ldc * ES), STORE_NT);
                     }
                     store_data_read_all(w);
 #pragma unroll

@@ -234,21 +234,19 @@ int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t K, in
     const int64_t b = batch < 1 ? 1 : batch;
     if (vec) {
         const int64_t tiles256 = cdiv(M, 256) * cdiv(N, 256) * b;
-        // several rounds with a short K: the persistent form, whose next
-        // tile's loads and MFMAs overlap the current tile's stores.  16-bit
-        // output up to K = 512 (at most 8 K tiles per output tile): 4-22%
-        // faster than the one-tile kernel over batches of 1024^2 to 8192^2
-        // products at K = 128..512, both layouts; even at 1024 and 1-12%
-        // slower from 2048 on (4 x 4096^2), where the one-tile kernel's wave
-        // priority and simpler loop win.  fp32 output only up to K = 128:
-        // there its 1 KiB-row staging through the 32 KiB the stages leave
-        // free stops the walk twice per 32 rows, and at K = 256..512 it was
-        // 3-35% slower than the one-tile kernel on five of six shapes; at
-        // K = 128 it ranged from 15% faster to 11% slower (the batched
-        // 32 x 2048^2 product: 1.5% faster).  Not in a single round.
+        // several rounds with K <= 512 (at most 8 K tiles per output tile):
+        // the persistent form, whose next tile's loads and MFMAs overlap the
+        // current tile's stores.  16-bit output: 4-22% faster than the
+        // one-tile kernel over batches of 1024^2 to 8192^2 products at
+        // K = 128..512, both layouts (even at 1024, 1-12% slower from 2048
+        // on, where the one-tile kernel's wave priority and simpler loop
+        // win).  fp32 output: 2-23% faster on every batched shape measured
+        // (32 x 2048^2, 16 x 2048^2, 128 x 1024^2, 8 x 4096^2, 4 x 4096^2),
+        // but 6-13% slower on a single 8192^2 product, so only for batches.
+        // Not in a single round.
         const int pid = config_by_name("256x256x64_s2_w2x4_m16p");
-        const int64_t kmax = c_type == TDG_F32 ? 128 : 512;
-        if (tiles256 >= 2 * cus && K > 0 && K <= kmax && !transa &&
+        const bool persist_ok = c_type != TDG_F32 || b >= 2;
+        if (tiles256 >= 2 * cus && K > 0 && K <= 512 && persist_ok && !transa &&
             config_ok(kConfigs[pid], transa, transb, vec, lda, ldb, ldc, c_type))
             return pid;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
