@@ -351,10 +351,9 @@ tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int6
         if (!split_pays(pl, cus)) pl = SplitPlan{tiles, 0, 1};
     }
     const size_t need = split_ws_bytes(cf, pl, cus);
-    if (need > split_ws_bound(cus)) pl = SplitPlan{tiles, 0, 1};   // (not reached: see split_ws_bound)
-    if (split_ws_bytes(cf, pl, cus) > ws_bytes)
+    if (need > ws_bytes)
         return fail(TDG_INVALID_VALUE, "workspace of %zu bytes is smaller than the %zu bytes this call needs", ws_bytes,
-                    split_ws_bytes(cf, pl, cus));
+                    need);
     const bool split = pl.split >= 2;
     a.ws_flags = split ? static_cast<int *>(ws) : nullptr;
     a.ws = split ? reinterpret_cast<float *>(static_cast<char *>(ws) + split_flag_bytes(cus)) : nullptr;
