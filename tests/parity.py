@@ -48,7 +48,7 @@ def check_exact(c_gpu: torch.Tensor, ref: np.ndarray, out_dtype: str, what=""):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     if out_dtype == "f32":
         expect = ref.astype(np.float32).astype(np.float64)
-        assert np.array_equal(expect, ref), "reference not exactly representable in fp32"
+        assert np.array_equal(expect, ref, equal_nan=True), "reference not exactly representable in fp32"
     else:
         expect = oracle.decode(oracle.encode(ref, out_dtype), out_dtype)
     bad = ~((got == expect) | (np.isnan(got) & np.isnan(expect)))

@@ -681,3 +681,61 @@ def test_batch_stride_past_32_bit(tdg):
     check_exact(cd.cpu(), ref, "f32", "huge batch stride")
     del abuf, cbuf
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# IEEE special values inside the operands
+# ---------------------------------------------------------------------------
+
+def _plant_specials(a, b, layout):
+    """Integer operands with NaN and infinities planted where the result does
+    not depend on the summation order: a NaN in A (its row of C is NaN), a
+    NaN in B (its column of C is NaN), one +inf in A (its row of C is +-inf,
+    or NaN where the matching B entry is 0), and +inf and -inf in one row of
+    A against equal B rows (NaN)."""
+    nan, inf = float("nan"), float("inf")
+    a = a.clone()
+    b = b.clone()
+    a[5, 7] = nan
+    a[100, 30] = inf
+    a[200, 40] = inf
+    a[200, 41] = -inf
+
+    def setb(k, n, v):
+        if layout == "nn":
+            b[k, n] = v
+        else:
+            b[n, k] = v
+    N = b.shape[1] if layout == "nn" else b.shape[0]
+    for n in range(N):
+        setb(40, n, 1.0)
+        setb(41, n, 1.0)
+    setb(50, 60, nan)
+    return a, b
+
+
+# (M, N, K, configuration or None for the automatic choice, with split-K)
+SPECIAL_CASES = [(384, 320, 256, "256x256x64_s2_w2x4_m16"), (384, 320, 256, "128x128x64_s4_w2x4_m16"),
+                 (384, 320, 256, "256x256x64_s2_w2x4_m16p"), (384, 320, 256, "256x256x64_s2_w2x4_lds"),
+                 (384, 320, 256, "64x64x64_w2x2_pred"), (1024, 1024, 4096, None)]
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("M,N,K,cfg", SPECIAL_CASES)
+@pytest.mark.parametrize("out_dtype", ["f16", "f32"])
+def test_ieee_special_values_propagate(tdg, layout, M, N, K, cfg, out_dtype):
+    """NaN and infinities in A and B reach C as IEEE arithmetic says (the
+    oracle sums the same bit patterns in binary64), through the one-tile,
+    persistent, 32 x 32 x 16, predicated and split-K paths."""
+    announce("ieee specials", layout, M, N, K, cfg, out_dtype)
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M + N + K + (layout == "tn"))
+    a, b = _plant_specials(a, b, layout)
+    config = -1 if cfg is None else tdg.config_names().index(cfg)
+    if cfg is None:
+        assert tdg.tdg_gemm_workspace_size(1 if layout == "tn" else 0, M, N, K, 1, 0) > 0, "should plan a K split"
+    c = gpu_gemm(tdg, a, b, layout, out_dtype, config=config)
+    ref = ref_gemm(a, b, "bf16", layout)
+    import numpy as np
+    assert np.isnan(ref[5]).all() and np.isnan(ref[:, 60]).all() and np.isnan(ref[200]).all()
+    assert np.isinf(ref[100]).any()
+    check_exact(c, ref, out_dtype, "ieee specials %s %s" % (layout, cfg))

@@ -296,3 +296,36 @@ def test_bad_arguments_rejected():
     C = np.zeros((2, 3))
     assert oracle.gemm_raw(0, 0, 2, 3, 3, p(A), 5, 0, p(B), 3, 0, p(C), 3, 0, 1) == 0
     assert np.array_equal(C, [[1, 2, 3], [4, 5, 6]])
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_ieee_special_values_term_by_term(layout, fmt):
+    """NaN and infinities in the operands: each output compared with its own
+    sum of products written out term by term in Python floats (IEEE binary64:
+    a NaN term or +inf plus -inf gives NaN, inf times 0 gives NaN, inf times
+    a nonzero value gives a signed infinity).  A NaN dropped by a masked path,
+    or an infinity cancelled by a reordered sum, fails here."""
+    M, N, K = 9, 7, 12
+    rng = np.random.default_rng(5)
+    Av = rng.integers(-2, 3, (M, K)).astype(np.float64)
+    Bv = rng.integers(-2, 3, (K, N)).astype(np.float64)
+    Av[1, 3] = np.nan
+    Av[4, 2] = np.inf
+    Bv[2, 0] = 0.0                      # inf * 0 at (4, 0)
+    Bv[2, 1:4] = [1.0, -2.0, 2.0]       # signed infinities at (4, 1..3)
+    Av[6, 5], Av[6, 8] = np.inf, -np.inf
+    Bv[5, :], Bv[8, :] = 1.0, 1.0       # +inf - inf across row 6
+    Bv[10, 4] = np.nan                  # column 4 all NaN
+    Bv[9, 6] = -np.inf
+    enc = f16_bits if fmt == "f16" else bf16_bits
+    Bstore = Bv if layout == "nn" else Bv.T
+    C = oracle.gemm(enc(Av), enc(np.ascontiguousarray(Bstore)), fmt, layout)
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += float(Av[i, k]) * float(Bv[k, j])
+            assert (np.isnan(s) and np.isnan(C[i, j])) or s == C[i, j], (i, j, s, C[i, j])
+    assert np.isnan(C[1]).all() and np.isnan(C[:, 4]).all() and np.isnan(C[6]).all() and np.isnan(C[4, 0])
+    assert np.isinf(C[4, 1:4]).all()
