@@ -204,3 +204,28 @@ def test_f8_determinism(tdg):
     c2 = gpu_f8(tdg, a, b, "e4m3", "e5m2", xa, xb, sa, sb, out="f32")
     assert torch.equal(c1, c2)
     assert np.isfinite(to_f64(c1)).all()
+
+
+@pytest.mark.parametrize("config", [0, 1])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_f8_ieee_special_values(tdg, config, scaled):
+    """NaN and infinities in 8-bit operands reach C as the oracle says: an
+    E4M3 NaN (S.1111.111) in A makes its row NaN; E5M2 infinities in B make
+    their column of C signed infinities (NaN where the A entry is 0); with
+    and without block and row scales."""
+    M, N, K = 96, 80, 256
+    for afmt, bfmt in (("e4m3", "e5m2"), ("e5m2", "e5m2")):
+        announce("f8 ieee", afmt, bfmt, "scaled" if scaled else "unscaled", "config", config)
+        a, b, xa, xb, _, _ = make_f8_inputs(M, N, K, afmt, bfmt, "ints", 77, block_scales=scaled, spread=1)
+        sa, sb = (pow2_scales(M, 5), pow2_scales(N, 6)) if scaled else (None, None)
+        a = a.copy()
+        b = b.copy()
+        a[3, 10] = 0x7F                      # NaN in either format
+        b[5, 20] = 0x7C                      # E5M2 +inf: column 5
+        b[9, 200] = 0xFC                     # E5M2 -inf: column 9
+        if afmt == "e5m2":
+            a[40, 100] = 0xFC                # E5M2 -inf in A: row 40
+        c = gpu_f8(tdg, a, b, afmt, bfmt, xa, xb, sa, sb, out="f32", config=config)
+        ref = oracle.gemm_f8(a, b, afmt, bfmt, xa=xa, xb=xb, sa=sa, sb=sb)
+        assert np.isnan(ref[3]).all() and np.isinf(ref[:, 5]).any() and np.isinf(ref[:, 9]).any()
+        check_exact(c, ref, "f32", "f8 ieee %s.%s" % (afmt, bfmt))
