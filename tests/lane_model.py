@@ -80,6 +80,7 @@ KERNELS = {
     2: ("16x16x32", True),     # 16 x 16 x 32 kernel: mfma(B, A)
     3: ("16x16x32", True),     # its persistent form
     4: ("16x16x32", True),     # its ping-pong form
+    5: ("16x16x32", True),     # its A-window form
     "f8": ("32x32x64f8", True),
 }
 
@@ -91,7 +92,7 @@ def parse_config(name):
     if parts[0] == "f8":
         kind, parts = "f8", parts[1:]
     else:
-        kind = {"lds": 1, "vec": 0, "pred": 0, "m16": 2, "m16p": 3, "m16pp": 4}[parts[-1]]
+        kind = {"lds": 1, "vec": 0, "pred": 0, "m16": 2, "m16p": 3, "m16pp": 4, "m16aw": 5}[parts[-1]]
     bm, bn = (int(v) for v in parts[0].split("x")[:2])
     wave = [p for p in parts if p.startswith("w") and "x" in p][0]
     wm, wn = (int(v) for v in wave[1:].split("x"))

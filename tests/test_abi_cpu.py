@@ -122,6 +122,10 @@ def test_config_selection(tdg):
     assert sel(1, 8192, 8192, 8192, c_type=2) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 4096, 4096, 4096) == "256x256x64_s2_w2x4_m16"
     assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16"
+    # TN with A rows off the 128-byte lines: the A-window form
+    assert sel(1, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16aw"
+    assert sel(1, 4096, 4096, 3000, lda=3008) == "256x256x64_s2_w2x4_m16"
+    assert sel(0, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16"
     # the persistent kernel: several rounds of 256 x 256 tiles and K <= 512
     # (fp32 output: batches only)
     assert sel(1, 2048, 2048, 128, batch=32) == "256x256x64_s2_w2x4_m16p"

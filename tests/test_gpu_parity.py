@@ -739,3 +739,55 @@ def test_ieee_special_values_propagate(tdg, layout, M, N, K, cfg, out_dtype):
     assert np.isnan(ref[5]).all() and np.isnan(ref[:, 60]).all() and np.isnan(ref[200]).all()
     assert np.isinf(ref[100]).any()
     check_exact(c, ref, out_dtype, "ieee specials %s %s" % (layout, cfg))
+
+
+# ---------------------------------------------------------------------------
+# A rows that do not start on 128-byte lines: the A-window form
+# ---------------------------------------------------------------------------
+
+# (layout, M, N, K, lda, byte offset of A past a 128-byte line)
+AWIN_CASES = [("nn", 520, 264, 3000, 3000, 0), ("tn", 300, 512, 1000, 1016, 16), ("nn", 257, 304, 136, 200, 48),
+              ("tn", 512, 520, 64, 72, 112), ("nn", 256, 256, 8, 8, 0), ("tn", 511, 257, 520, 600, 80)]
+
+
+@pytest.mark.parametrize("layout,M,N,K,lda,a_off", AWIN_CASES)
+@pytest.mark.parametrize("auto", [False, True])
+def test_a_window_exact(tdg, layout, M, N, K, lda, a_off, auto):
+    """A stored with row stride lda (rows off the 128-byte lines) starting
+    a_off bytes past a line, NaN in every byte between the rows and before
+    the first: the A-window configuration (forced, or the library's choice)
+    reads exactly the rows' K elements -- any other byte would make a sum
+    NaN -- and the result is bit-exact."""
+    announce("a window", layout, M, N, K, lda, a_off, "auto" if auto else "forced")
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=M + N + K + lda)
+    pre = 64 + a_off // 2                               # elements before A (a_off bytes past a line)
+    store = torch.full((pre + M * lda + 64,), float("nan"), dtype=torch.bfloat16)
+    view = store.as_strided((M, K), (lda, 1), pre)
+    view.copy_(a)
+    sd = store.cuda()
+    assert sd.data_ptr() % 128 == 0
+    ad = sd.as_strided((M, K), (lda, 1), pre)
+    bd = b.cuda()
+    if auto:
+        c = tdg.gemm(ad, bd, layout=layout, out_dtype=torch.float32)
+        if M * N >= 256 * 256 * 256 and (lda * 2) % 128:
+            assert tdg.config_names()[tdg.select_config(ad, bd, layout, torch.float32)].endswith("_m16aw")
+    else:
+        cfg = tdg.config_names().index("256x256x64_s2_w2x4_m16aw")
+        c = tdg.gemm(ad, bd, layout=layout, out_dtype=torch.float32, config=cfg)
+    torch.cuda.synchronize()
+    check_exact(c.cpu(), ref_gemm(a, b, "bf16", layout), "f32", "a window %s %dx%dx%d lda %d" % (layout, M, N, K, lda))
+
+
+def test_a_window_choice(tdg):
+    """The library picks the A-window form for TN products of at least one
+    round of 256 x 256 tiles whose A rows are off the 128-byte lines, and the
+    plain form for NN and for aligned rows."""
+    names = tdg.config_names()
+    def pick(layout, M, N, K, lda):
+        ad = torch.empty(M, lda, dtype=torch.float16, device="cuda")[:, :K]
+        bd = torch.empty((N, K) if layout == "tn" else (K, N), dtype=torch.float16, device="cuda")
+        return names[tdg.select_config(ad, bd, layout, torch.float16)]
+    assert pick("tn", 4096, 4096, 3000, 3000).endswith("_m16aw")
+    assert pick("tn", 4096, 4096, 3000, 3008) == "256x256x64_s2_w2x4_m16"
+    assert pick("nn", 4095, 5000, 3000, 3000) == "256x256x64_s2_w2x4_m16"

@@ -53,7 +53,9 @@ struct F8Args {
 // kernel built on 16 x 16 x 32 MFMAs (aligned operands, BK 64 or 32); KIND 3 = its
 // persistent form (one workgroup per CU walking its tiles, K > 0); KIND 4 =
 // its ping-pong form (two groups of four waves alternating a memory phase
-// and an MFMA phase; A stored M x K only).
+// and an MFMA phase; A stored M x K only); KIND 5 = the 16 x 16 x 32 kernel
+// with A's rows loaded as aligned 128-byte chunks into a ring of three slots
+// (for an A whose rows do not start on 128-byte lines; A stored M x K only).
 #define TDG_CONFIG_LIST(X)                                                   \
     X(0, 1, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_lds")           \
     X(1, 1, 256, 256, 32, 3, 2, 4, true, "256x256x32_s3_w2x4_lds")           \
@@ -72,7 +74,8 @@ struct F8Args {
     X(14, 3, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16p")         \
     X(15, 2, 256, 256, 64, 2, 2, 2, true, "256x256x64_s2_w2x2_m16")          \
     X(16, 4, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16pp")        \
-    X(17, 2, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_m16")
+    X(17, 2, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_m16")          \
+    X(18, 5, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16aw")
 
 // 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
 #define TDG_F8_CONFIG_LIST(X)                                   \

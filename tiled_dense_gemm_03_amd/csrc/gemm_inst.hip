@@ -24,6 +24,10 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
         static_assert(BK == 64 || BK == 32, "the 16x16x32 kernel uses K tiles of 64 or 32");
         hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, false, BK>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
+    } else if constexpr (KIND == 5) {
+        static_assert(BK == 64 && ST == 2, "the A window: K tiles of 64, two B stages");
+        hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, false, 64, true>),
+                           dim3((unsigned)grid), dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 4) {
         static_assert(BK == 64, "the 16x16x32 kernel uses K tiles of 64");
         hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, true>), dim3((unsigned)grid),
@@ -41,9 +45,9 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
 template <int KIND, int BM, int BN, int BK, int ST, int WM, int WN, bool TA, bool VEC>
 static hipError_t launch_ct(int ct, const GemmArgs &a, int64_t grid, hipStream_t s) {
     constexpr bool TB = TDG_TRANSB != 0;
-    if constexpr ((KIND >= 1 && !TB && BN / 8 < 16) || (TA && (KIND < 2 || KIND == 4 || BM / 8 < 16))) {
+    if constexpr ((KIND >= 1 && !TB && BN / 8 < 16) || (TA && (KIND < 2 || KIND >= 4 || BM / 8 < 16))) {
         // an MC operand needs the direct-to-LDS kernels with >= 128-wide
-        // rows; the ping-pong form takes an A stored M x K only
+        // rows; the ping-pong and A-window forms take an A stored M x K only
         return hipErrorInvalidValue;
     } else {
         switch (ct) {

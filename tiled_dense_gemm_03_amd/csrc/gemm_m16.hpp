@@ -136,7 +136,7 @@ __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) 
 // TRANSA: false = A stored M x K (KC), true = A stored K x M (MC).
 // TRANSB: false = B stored K x N (MC), true = B stored N x K (KC).
 template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT, bool PP = false,
-          int BKT = 64>
+          int BKT = 64, bool AWIN = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     constexpr int BK = BKT, KS = BK / 32, KG = BK / GRAN, BNG = BN / GRAN, BMG = BM / GRAN;
     static_assert(BK == 64 || (BK == 32 && !PP), "K tiles of 64, or of 32 (one MFMA K step per stage)");
@@ -167,9 +167,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     constexpr bool ASM_ACC = (BM / WM / 16) * (BN / WN / 16) * 4 > 160;
     static_assert(!PP || (WM == 2 && WN == 4 && STAGES == 2 && !ASM_ACC),
                   "the ping-pong schedule: two groups of four waves (one per SIMD each), two stages");
+    // AWIN: A (stored M x K) whose rows do not start on 128-byte lines is
+    // loaded as whole aligned 128-byte chunks of each row into a ring of
+    // three A slots (B keeps two stages); see the A-window loop below.
+    static_assert(!AWIN || (!TRANSA && BK == 64 && STAGES == 2 && !PP && !ASM_ACC),
+                  "the A window: A stored M x K, K tiles of 64, two B stages");
+    constexpr int LDS_SLOTS = AWIN ? 3 * A_SLOTS + 2 * B_SLOTS : STAGES * STAGE;
+    static_assert(LDS_SLOTS * 16 <= 160 * 1024, "LDS budget");
 
-    __shared__ u32x4 smem[STAGES * STAGE];
-    __shared__ int sk_last;
+    __shared__ u32x4 smem[LDS_SLOTS];
     auto stage_ptr = [&](auto tag) -> u32x4 * { return smem + decltype(tag)::value * STAGE; };
 
     // ---- work item: a whole tile, or one K slice of a split tile ----
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         }
         if (g == 0) __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-    } else if (kt_end > kt_begin) {
+    } else if (!AWIN && kt_end > kt_begin) {
         static_for<0, STAGES>([&](auto s) { issue_to(kt_begin + decltype(s)::value, stage_ptr(s)); });
         // K tiles of 64: the first stage; of 32: the first two (the second
         // one's fragments are read during the first step)
@@ -443,6 +449,113 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     int s_cur = 0;
     if constexpr (PP) {
         // (the ping-pong loop ran above)
+    } else if constexpr (AWIN) {
+        // ---- A window: rows of A that do not start on a 128-byte line ----
+        // A row whose K run of a tile (128 bytes) starts s bytes past a line
+        // boundary touches two lines per load instruction instead of one.
+        // Here each row is loaded as its own aligned 128-byte chunks instead:
+        // chunk c of row r holds the bytes [128 c, 128 c + 128) of the row's
+        // line-aligned stream, i.e. elements 64 c - s/2 .. 64 c - s/2 + 63.
+        // Tile kt's elements of the row then lie in chunks kt and kt + 1, so
+        // three chunk slots make a ring: chunks kt, kt + 1 in use and kt + 2
+        // arriving (loaded during tile kt - 1), and chunk kt + 3 loaded into
+        // chunk kt's slot once tile kt is read.  B keeps two stages.  The
+        // shift s is a multiple of 16 bytes (lda is a multiple of 8) and
+        // depends on the row only modulo 8, so every lane has one shift for
+        // its loads and one for its fragment reads.  Elements before the row's
+        // first or past its K-th read as zeros.  LDS: A slot c % 3 at
+        // (c % 3) * A_SLOTS (granule g of row r at g ^ kx16(r), as the other
+        // K-contiguous layouts), B stage t % 2 after the three A slots.
+        const char *Abytes = reinterpret_cast<const char *>(Atile);
+        const int s_ld = (int)(((uintptr_t)Abytes + (uintptr_t)(kc_row * lda * 2)) & 127);
+        const int aw_e0 = 8 * kc_g - s_ld / 2;          // element of the lane's granule in chunk 0
+        const uint32_t aw_off = (uint32_t)(kc_row * lda * 2 + 16 * kc_g - s_ld + 128);
+        const int d_rd = (int)((((uintptr_t)Abytes + (uintptr_t)(fr * lda * 2)) & 127) >> 4);
+        int aw_b[KS], aw_co[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int pp = 4 * ks + fg + d_rd;            // granule in the two-chunk window
+            aw_co[ks] = pp >> 3;
+            aw_b[ks] = (wave_m * WTM + fr) * KG + ((pp & 7) ^ kxor<KG>(fr));
+        }
+        u32x4 *const bstages = smem + 3 * A_SLOTS;
+        auto dma_a = [&](auto qtag, int c) {              // A chunk c (all K tiles' rows) into slot c % 3
+            constexpr int q = decltype(qtag)::value;
+            const uint32_t base = lds_addr_of(smem + (c % 3) * A_SLOTS) + (uint32_t)wave * 1024u;
+            const u32x4 rs = rsrc_words_n(Abytes + 128 * (int64_t)(c - 1),
+                                          records_of(64 * (int64_t)(1 - c) + (int64_t)(a_rows - 1) * lda + K));
+            const int e = 64 * c + aw_e0;
+            const uint32_t off = (e >= 0 && e + GRAN <= K) ? aw_off + (uint32_t)q * a_qs : OOB_OFFSET;
+            dma16_sel<false, (uint32_t)(q * NW) * 1024u>(rs, off, base);
+        };
+        auto dma_b = [&](auto qtag, int kt, u32x4 *bst) {  // B load qb of K tile kt into a B stage
+            constexpr int qb = decltype(qtag)::value;
+            const int k0 = kt * BK;
+            const uint32_t base = lds_addr_of(bst) + (uint32_t)wave * 1024u;
+            if constexpr (TRANSB) {
+                const u32x4 rs = rsrc_words_n(Btile + k0, records_of((int64_t)(b_rows - 1) * ldb + K - k0));
+                const uint32_t off = (k0 < kc_klim ? b_lane[0] : OOB_OFFSET) + (uint32_t)qb * b_qs;
+                dma16_sel<false, (uint32_t)(qb * NW * 1024)>(rs, off, base);
+            } else {
+                const u32x4 rs = rsrc_words_n(Btile + (int64_t)k0 * ldb,
+                                              records_of((int64_t)(K - k0 - 1) * ldb + (N - n0)));
+                const uint32_t off = b_lane[qb % NVB] + (uint32_t)qb * b_qs;
+                dma16_sel<false, (uint32_t)(qb * NW * 1024)>(rs, off, base);
+            }
+        };
+        // K step ks of tile kt (chunks kt, kt + 1; B stage bst): fragment d
+        auto frag_w = [&](auto dtag, int kt, const u32x4 *bst, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
+            constexpr int d = decltype(dtag)::value;
+            if constexpr (d < RM) {
+                const int slot = (kt + aw_co[ks]) % 3;
+                af[d] = smem[slot * A_SLOTS + aw_b[ks] + d * 16 * KG];
+            } else {
+                frag_op(dtag, bst - A_SLOTS, ks, af, bf);  // (frag_op reads B at its argument + A_SLOTS)
+            }
+        };
+        if (kt_end > kt_begin) {
+            // chunks kt_begin, kt_begin + 1 and B tile kt_begin first, then
+            // chunk kt_begin + 2 and B tile kt_begin + 1
+            static_for<0, QA>([&](auto q) { dma_a(q, kt_begin); });
+            static_for<0, QA>([&](auto q) { dma_a(q, kt_begin + 1); });
+            static_for<0, QB>([&](auto q) { dma_b(q, kt_begin, bstages); });
+            static_for<0, QA>([&](auto q) { dma_a(q, kt_begin + 2); });
+            static_for<0, QB>([&](auto q) { dma_b(q, kt_begin + 1, bstages + B_SLOTS); });
+            wait_vm_lgkm0<QA + QB>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            static_for<0, NDS>([&](auto d) { frag_w(d, kt_begin, bstages, 0, af[0], bf[0]); });
+        }
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int rel = kt - kt_begin;
+            u32x4 *bcur = bstages + (rel & 1) * B_SLOTS;
+            u32x4 *bnxt = bstages + ((rel + 1) & 1) * B_SLOTS;
+            static_for<0, NDS>([&](auto d) { frag_w(d, kt, bcur, 1, af[1], bf[1]); });
+#pragma unroll
+            for (int i = 0; i < RM; ++i)
+#pragma unroll
+                for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[0][j], af[0][i], acc[i][j]);
+            interleave_hint<NMF, NDS>();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if constexpr (TRANSB) wave_priority<1>();
+            constexpr int NSUB = NDMA;
+            static_for<0, NSUB>([&](auto sub) {
+                constexpr int s0 = decltype(sub)::value;
+                static_for<s0 * NMF / NSUB, (s0 + 1) * NMF / NSUB>([&](auto m) {
+                    constexpr int i = decltype(m)::value / RN, j = decltype(m)::value % RN;
+                    acc[i][j] = mfma_16x16x32<AB>(bf[1][j], af[1][i], acc[i][j]);
+                });
+                static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>(
+                    [&](auto d) { frag_w(d, kt + 1, bnxt, 0, af[0], bf[0]); });
+                if constexpr (s0 < QA) dma_a(sub, kt + 3);
+                else dma_b(std::integral_constant<int, s0 - QA>{}, kt + 2, bcur);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (TRANSB) wave_priority<0>();
+        }
     } else if constexpr (BK == 32) {
         // K tiles of 32: one MFMA K step per stage and one barrier per step.
         // Step kt's MFMAs run interleaved with the fragment reads of step
@@ -582,11 +695,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);                     // this wave's partial has landed
         __syncthreads();                                   // ... and every wave's
+        // (the flag lives in the first LDS word: every wave's loads have
+        // landed, so no direct load can still write there)
+        int *sk_last = reinterpret_cast<int *>(smem);
         if (tid == 0)
-            sk_last = __hip_atomic_fetch_add(p.ws_flags + split_tile, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            *sk_last = __hip_atomic_fetch_add(p.ws_flags + split_tile, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) == S - 1;
         __syncthreads();
-        if (!sk_last) return;
+        if (!*sk_last) return;
         // Sum slice by slice, CH accumulators at a time, so that CH loads are
         // in flight per wait.
         constexpr int NACC = RM * RN, CH = 8;

@@ -118,7 +118,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // K x N), rows of at least 16 granules in LDS.
 bool config_ok(const Config &cf, int transa, int transb, bool vec, int64_t lda, int64_t ldb, int64_t ldc,
                int c_type) {
-    if (transa && cf.kind != 2) return false;
+    if (transa && cf.kind != 2) return false;        // (the other kinds read A stored M x K only)
     if (!cf.vec) return true;
     if (!vec) return false;
     if (cf.kind < 1) return true;
@@ -131,6 +131,10 @@ bool config_ok(const Config &cf, int transa, int transb, bool vec, int64_t lda, 
     if (transa && cf.bm / 8 < 16) return false;
     return true;
 }
+
+// The one-tile 16 x 16 x 32 kernel, plain or with the A window: the kinds
+// that take split-K and partial-round schedules.
+bool one_tile_m16(const Config &cf) { return cf.kind == 2 || cf.kind == 5; }
 
 int config_by_name(const char *name) {
     for (int i = 0; i < kNumConfigs; ++i)
@@ -249,6 +253,18 @@ int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t K, in
         if (tiles256 >= 2 * cus && K > 0 && K <= 512 && persist_ok && !transa &&
             config_ok(kConfigs[pid], transa, transb, vec, lda, ldb, ldc, c_type))
             return pid;
+        // one round or more, TN: rows of A that do not start on 128-byte
+        // lines (lda not a multiple of 64) take the A-window form, which loads
+        // each row as aligned 128-byte chunks (the kernel works out every
+        // row's shift from the actual addresses, so this is only the
+        // choice).  Measured against the plain form: TN 8192^2 x 3000 and
+        // 4095 x 5000 x 3000 -5 to -7%, 4096^2 x 2000 and x 4000 -4 to -5%,
+        // 8192 x 4096 x 1000 (fp32 out) -4%; NN within +-1.5% either way
+        // (lda 1000 to 5000), so NN keeps the plain form.
+        const int aw = config_by_name("256x256x64_s2_w2x4_m16aw");
+        if (tiles256 >= cus && transb && !transa && (lda * 2) % 128 != 0 &&
+            config_ok(kConfigs[aw], transa, transb, vec, lda, ldb, ldc, c_type))
+            return aw;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
         if (tiles256 >= cus && config_ok(kConfigs[id], transa, transb, vec, lda, ldb, ldc, c_type)) return id;
         const int mid = config_by_name("128x128x64_s4_w2x4_m16");
@@ -346,7 +362,7 @@ tdg_status launch(int config, int transa, int transb, int64_t M, int64_t N, int6
     SplitPlan pl{tiles, 0, 1};
     if (plan != nullptr) {
         pl = *plan;
-    } else if (cf.kind == 2 && ws != nullptr) {
+    } else if (one_tile_m16(cf) && ws != nullptr) {
         pl = plan_split(tiles, cdiv(K, cf.bk), cus);
         if (!split_pays(pl, cus)) pl = SplitPlan{tiles, 0, 1};
     }
@@ -509,7 +525,7 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
     // of 64 small tiles (K 32768), 0.98 with a rest of 128, 1.03 and 1.13
     // with rests of 128 and 256 (4095 x 5000 x 3000): the merge of 256 x 256
     // partial tiles costs more than a well-filled rest round.
-    if (automatic && !tuned && cf.kind == 2 && batch == 1 && ws != nullptr) {
+    if (automatic && !tuned && one_tile_m16(cf) && batch == 1 && ws != nullptr) {
         const SplitPlan rp = plan_round_split(cdiv(M, cf.bm) * cdiv(N, cf.bn), cdiv(K, cf.bk), cus);
         if (rp.split >= 2 && split_ws_bytes(cf, rp, cus) <= ws_bytes) {
             bool cols = true;
@@ -783,7 +799,7 @@ size_t tdg_gemm_workspace_size(int transb, int64_t M, int64_t N, int64_t K, int6
     const int id = tdg::choose(0, transb, true, M, N, K, batch, K, transb ? K : N, N, TDG_F32, cus);
     if (id < 0) return 0;
     const tdg::Config &cf = tdg::kConfigs[id];
-    if (cf.kind != 2) return 0;
+    if (!tdg::one_tile_m16(cf)) return 0;
     const int64_t tiles = tdg::cdiv(M, cf.bm) * tdg::cdiv(N, cf.bn) * batch;
     if (batch == 1 && tiles > cus) {
         // (an upper bound: run() may serve the problem with the cut instead)
