@@ -131,10 +131,13 @@ __device__ __forceinline__ int kxor(int r) { return KG == 8 ? (r >> 1) & 7 : (r 
 __device__ __forceinline__ int nx16(int k) { return 4 * (k & 3) + 2 * ((k >> 3) & 1); }  // NN-B XOR
 
 // BM x BN workgroup tile, WM x WN waves of (BM/WM) x (BN/WN), K tiles of 64
-// in STAGES LDS stages.
+// (BKT = 32: of 32) in STAGES LDS stages.
 //
 // TRANSA: false = A stored M x K (KC), true = A stored K x M (MC).
 // TRANSB: false = B stored K x N (MC), true = B stored N x K (KC).
+// PP: the ping-pong schedule (two wave groups alternating memory and MFMA
+// phases).  AWIN: the A window (A rows loaded as line-aligned chunks into a
+// ring of three slots, for rows that do not start on 128-byte lines).
 template <int BM, int BN, int WM, int WN, int STAGES, bool TRANSA, bool TRANSB, int AB, int CT, bool PP = false,
           int BKT = 64, bool AWIN = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
