@@ -126,6 +126,8 @@ def test_config_selection(tdg):
     assert sel(1, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16aw"
     assert sel(1, 4096, 4096, 3000, lda=3008) == "256x256x64_s2_w2x4_m16"
     assert sel(0, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16"
+    assert sel(1, 1024, 1024, 3000) == "128x128x64_s4_w2x4_m16aw"
+    assert sel(0, 1024, 1024, 3000) == "128x128x64_s4_w2x4_m16"
     # the persistent kernel: several rounds of 256 x 256 tiles and K <= 512
     # (fp32 output: batches only)
     assert sel(1, 2048, 2048, 128, batch=32) == "256x256x64_s2_w2x4_m16p"

@@ -791,3 +791,23 @@ def test_a_window_choice(tdg):
     assert pick("tn", 4096, 4096, 3000, 3000).endswith("_m16aw")
     assert pick("tn", 4096, 4096, 3000, 3008) == "256x256x64_s2_w2x4_m16"
     assert pick("nn", 4095, 5000, 3000, 3000) == "256x256x64_s2_w2x4_m16"
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 16008), (4352, 4352, 1000), (4095, 5000, 3000)])
+def test_a_window_split_schedules_exact(tdg, M, N, K):
+    """TN products with A rows off the 128-byte lines through the library's
+    own schedules: split-K on the 128 x 128 A-window form (few tiles, long
+    K), the one-launch partial round or the cut on the 256 x 256 one;
+    bit-exact and the same bits on a second call."""
+    announce("a window schedules", M, N, K)
+    assert (K * 2) % 128 != 0
+    a, b = make_inputs(M, N, K, "tn", "bf16", "ints", seed=M + N + K + 5)
+    ad, bd = a.cuda(), b.cuda()
+    assert "_m16aw" in tdg.config_names()[tdg.select_config(ad, bd, "tn", torch.float32)]
+    c1 = tdg.gemm(ad, bd, layout="tn", out_dtype=torch.float32)
+    c2 = tdg.gemm(ad, bd, layout="tn", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    rows = sample_rows(M) if M * N * K > 2 ** 31 else None
+    ref = ref_gemm(a, b, "bf16", "tn", rows=rows)
+    check_exact(c1.cpu()[rows] if rows is not None else c1.cpu(), ref, "f32", "a window schedules %dx%dx%d" % (M, N, K))

@@ -75,7 +75,8 @@ struct F8Args {
     X(15, 2, 256, 256, 64, 2, 2, 2, true, "256x256x64_s2_w2x2_m16")          \
     X(16, 4, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16pp")        \
     X(17, 2, 256, 256, 32, 4, 2, 4, true, "256x256x32_s4_w2x4_m16")          \
-    X(18, 5, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16aw")
+    X(18, 5, 256, 256, 64, 2, 2, 4, true, "256x256x64_s2_w2x4_m16aw")        \
+    X(19, 5, 128, 128, 64, 4, 2, 4, true, "128x128x64_s4_w2x4_m16aw")
 
 // 8-bit configurations: X(id, BM, BN, STAGES, WM, WN, name), K tiles of 128.
 #define TDG_F8_CONFIG_LIST(X)                                   \

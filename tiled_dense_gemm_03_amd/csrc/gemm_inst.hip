@@ -25,7 +25,7 @@ static void launch_one(const GemmArgs &a, int64_t grid, hipStream_t s) {
         hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, false, BK>), dim3((unsigned)grid),
                            dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 5) {
-        static_assert(BK == 64 && ST == 2, "the A window: K tiles of 64, two B stages");
+        static_assert(BK == 64, "the A window: K tiles of 64");
         hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, WM, WN, ST, TA, TB, TDG_AB, CT, false, 64, true>),
                            dim3((unsigned)grid), dim3(WM * WN * 64), 0, s, a);
     } else if constexpr (KIND == 4) {

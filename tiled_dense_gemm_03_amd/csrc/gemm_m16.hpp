@@ -173,9 +173,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
     // AWIN: A (stored M x K) whose rows do not start on 128-byte lines is
     // loaded as whole aligned 128-byte chunks of each row into a ring of
     // three A slots (B keeps two stages); see the A-window loop below.
-    static_assert(!AWIN || (!TRANSA && BK == 64 && STAGES == 2 && !PP && !ASM_ACC),
-                  "the A window: A stored M x K, K tiles of 64, two B stages");
-    constexpr int LDS_SLOTS = AWIN ? 3 * A_SLOTS + 2 * B_SLOTS : STAGES * STAGE;
+    static_assert(!AWIN || (!TRANSA && BK == 64 && !PP && !ASM_ACC), "the A window: A stored M x K, K tiles of 64");
+    constexpr int AW_R = STAGES + 1;                  // A chunk slots of the A window
+    constexpr int LDS_SLOTS = AWIN ? AW_R * A_SLOTS + STAGES * B_SLOTS : STAGES * STAGE;
     static_assert(LDS_SLOTS * 16 <= 160 * 1024, "LDS budget");
 
     __shared__ u32x4 smem[LDS_SLOTS];
@@ -460,15 +460,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         // chunk c of row r holds the bytes [128 c, 128 c + 128) of the row's
         // line-aligned stream, i.e. elements 64 c - s/2 .. 64 c - s/2 + 63.
         // Tile kt's elements of the row then lie in chunks kt and kt + 1, so
-        // three chunk slots make a ring: chunks kt, kt + 1 in use and kt + 2
-        // arriving (loaded during tile kt - 1), and chunk kt + 3 loaded into
-        // chunk kt's slot once tile kt is read.  B keeps two stages.  The
-        // shift s is a multiple of 16 bytes (lda is a multiple of 8) and
-        // depends on the row only modulo 8, so every lane has one shift for
-        // its loads and one for its fragment reads.  Elements before the row's
-        // first or past its K-th read as zeros.  LDS: A slot c % 3 at
-        // (c % 3) * A_SLOTS (granule g of row r at g ^ kx16(r), as the other
-        // K-contiguous layouts), B stage t % 2 after the three A slots.
+        // STAGES + 1 chunk slots make a ring: chunks kt, kt + 1 in use,
+        // kt + 2 .. kt + STAGES arriving, and chunk kt + STAGES + 1 loaded
+        // into chunk kt's slot once tile kt is read (with B tile kt + STAGES
+        // into tile kt's B stage).  The shift s is a multiple of 16 bytes
+        // (lda is a multiple of 8) and depends on the row only modulo 8, so
+        // every lane has one shift for its loads and one for its fragment
+        // reads.  Elements before the row's first or past its K-th read as
+        // zeros.  LDS: A slot c % (STAGES + 1) (granule g of row r at
+        // g ^ kx16(r), as the other K-contiguous layouts), then the B stages.
         const char *Abytes = reinterpret_cast<const char *>(Atile);
         const int s_ld = (int)(((uintptr_t)Abytes + (uintptr_t)(kc_row * lda * 2)) & 127);
         const int aw_e0 = 8 * kc_g - s_ld / 2;          // element of the lane's granule in chunk 0
@@ -481,10 +481,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
             aw_co[ks] = pp >> 3;
             aw_b[ks] = (wave_m * WTM + fr) * KG + ((pp & 7) ^ kxor<KG>(fr));
         }
-        u32x4 *const bstages = smem + 3 * A_SLOTS;
-        auto dma_a = [&](auto qtag, int c) {              // A chunk c (all K tiles' rows) into slot c % 3
+        u32x4 *const bstages = smem + AW_R * A_SLOTS;
+        auto dma_a = [&](auto qtag, int c) {              // A chunk c into slot c % AW_R
             constexpr int q = decltype(qtag)::value;
-            const uint32_t base = lds_addr_of(smem + (c % 3) * A_SLOTS) + (uint32_t)wave * 1024u;
+            const uint32_t base = lds_addr_of(smem + (c % AW_R) * A_SLOTS) + (uint32_t)wave * 1024u;
             const u32x4 rs = rsrc_words_n(Abytes + 128 * (int64_t)(c - 1),
                                           records_of(64 * (int64_t)(1 - c) + (int64_t)(a_rows - 1) * lda + K));
             const int e = 64 * c + aw_e0;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         auto frag_w = [&](auto dtag, int kt, const u32x4 *bst, int ks, u32x4 (&af)[RM], u32x4 (&bf)[RN]) {
             constexpr int d = decltype(dtag)::value;
             if constexpr (d < RM) {
-                const int slot = (kt + aw_co[ks]) % 3;
+                const int slot = (kt + aw_co[ks]) % AW_R;
                 af[d] = smem[slot * A_SLOTS + aw_b[ks] + d * 16 * KG];
             } else {
                 frag_op(dtag, bst - A_SLOTS, ks, af, bf);  // (frag_op reads B at its argument + A_SLOTS)
@@ -518,21 +518,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         };
         if (kt_end > kt_begin) {
             // chunks kt_begin, kt_begin + 1 and B tile kt_begin first, then
-            // chunk kt_begin + 2 and B tile kt_begin + 1
+            // for each later stage s, chunk kt_begin + s + 1 and B tile
+            // kt_begin + s; the first group is waited for
             static_for<0, QA>([&](auto q) { dma_a(q, kt_begin); });
             static_for<0, QA>([&](auto q) { dma_a(q, kt_begin + 1); });
             static_for<0, QB>([&](auto q) { dma_b(q, kt_begin, bstages); });
-            static_for<0, QA>([&](auto q) { dma_a(q, kt_begin + 2); });
-            static_for<0, QB>([&](auto q) { dma_b(q, kt_begin + 1, bstages + B_SLOTS); });
-            wait_vm_lgkm0<QA + QB>();
+            static_for<1, STAGES>([&](auto st) {
+                constexpr int sg = decltype(st)::value;
+                static_for<0, QA>([&](auto q) { dma_a(q, kt_begin + sg + 1); });
+                static_for<0, QB>([&](auto q) { dma_b(q, kt_begin + sg, bstages + sg * B_SLOTS); });
+            });
+            wait_vm_lgkm0<(STAGES - 1) * NDMA>();
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             static_for<0, NDS>([&](auto d) { frag_w(d, kt_begin, bstages, 0, af[0], bf[0]); });
         }
+        int b_cur = 0;
         for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int rel = kt - kt_begin;
-            u32x4 *bcur = bstages + (rel & 1) * B_SLOTS;
-            u32x4 *bnxt = bstages + ((rel + 1) & 1) * B_SLOTS;
+            const int b_nxt = (b_cur + 1 == STAGES) ? 0 : b_cur + 1;
+            u32x4 *bcur = bstages + b_cur * B_SLOTS;
+            u32x4 *bnxt = bstages + b_nxt * B_SLOTS;
             static_for<0, NDS>([&](auto d) { frag_w(d, kt, bcur, 1, af[1], bf[1]); });
 #pragma unroll
             for (int i = 0; i < RM; ++i)
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
                 for (int j = 0; j < RN; ++j) acc[i][j] = mfma_16x16x32<AB>(bf[0][j], af[0][i], acc[i][j]);
             interleave_hint<NMF, NDS>();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_vm_lgkm0<0>();
+            wait_vm_lgkm0<(STAGES - 2) * NDMA>();
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if constexpr (TRANSB) wave_priority<1>();
@@ -553,11 +558,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
                 });
                 static_for<s0 * NDS / NSUB, (s0 + 1) * NDS / NSUB>(
                     [&](auto d) { frag_w(d, kt + 1, bnxt, 0, af[0], bf[0]); });
-                if constexpr (s0 < QA) dma_a(sub, kt + 3);
-                else dma_b(std::integral_constant<int, s0 - QA>{}, kt + 2, bcur);
+                if constexpr (s0 < QA) dma_a(sub, kt + STAGES + 1);
+                else dma_b(std::integral_constant<int, s0 - QA>{}, kt + STAGES, bcur);
                 __builtin_amdgcn_sched_barrier(0);
             });
             if constexpr (TRANSB) wave_priority<0>();
+            b_cur = b_nxt;
         }
     } else if constexpr (BK == 32) {
         // K tiles of 32: one MFMA K step per stage and one barrier per step.

@@ -142,6 +142,14 @@ int config_by_name(const char *name) {
     return -1;
 }
 
+// Whether a TN product's A rows start off the 128-byte lines (lda not a
+// multiple of 64 elements), where the A-window forms pay: measured against
+// the plain forms, TN 256 x 256 tiles 4-7% faster on five shapes and
+// 128 x 128 tiles 8% on two (both operands K-contiguous and off the lines);
+// NN within +-1.5% for 256 x 256 tiles and up to 12% slower for 128 x 128
+// tiles, so NN keeps the plain forms.
+bool a_window_pays(int transa, int transb, int64_t lda) { return transb && !transa && (lda * 2) % 128 != 0; }
+
 // Split-K schedule for the 16x16x32 kernel (NineToothed primer s4 names the
 // alternative to keeping K inside one program: split it, at the price of a
 // merge step).  With `cus` workgroups running at once, a problem of fewer
@@ -253,20 +261,19 @@ int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t K, in
         if (tiles256 >= 2 * cus && K > 0 && K <= 512 && persist_ok && !transa &&
             config_ok(kConfigs[pid], transa, transb, vec, lda, ldb, ldc, c_type))
             return pid;
-        // one round or more, TN: rows of A that do not start on 128-byte
-        // lines (lda not a multiple of 64) take the A-window form, which loads
-        // each row as aligned 128-byte chunks (the kernel works out every
-        // row's shift from the actual addresses, so this is only the
-        // choice).  Measured against the plain form: TN 8192^2 x 3000 and
-        // 4095 x 5000 x 3000 -5 to -7%, 4096^2 x 2000 and x 4000 -4 to -5%,
-        // 8192 x 4096 x 1000 (fp32 out) -4%; NN within +-1.5% either way
-        // (lda 1000 to 5000), so NN keeps the plain form.
+        // one round or more, TN with A rows off the 128-byte lines: the
+        // A-window form, which loads each row as aligned 128-byte chunks (the
+        // kernel works out every row's shift from the actual addresses, so
+        // this is only the choice; a_window_pays has the measurements)
         const int aw = config_by_name("256x256x64_s2_w2x4_m16aw");
-        if (tiles256 >= cus && transb && !transa && (lda * 2) % 128 != 0 &&
+        if (tiles256 >= cus && a_window_pays(transa, transb, lda) &&
             config_ok(kConfigs[aw], transa, transb, vec, lda, ldb, ldc, c_type))
             return aw;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
         if (tiles256 >= cus && config_ok(kConfigs[id], transa, transb, vec, lda, ldb, ldc, c_type)) return id;
+        const int mid_aw = config_by_name("128x128x64_s4_w2x4_m16aw");
+        if (a_window_pays(transa, transb, lda) && config_ok(kConfigs[mid_aw], transa, transb, vec, lda, ldb, ldc, c_type))
+            return mid_aw;
         const int mid = config_by_name("128x128x64_s4_w2x4_m16");
         if (config_ok(kConfigs[mid], transa, transb, vec, lda, ldb, ldc, c_type)) return mid;
         if (transa) return -1;
@@ -538,7 +545,8 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
         }
     }
     if (automatic && !tuned && cf.kind >= 2 && batch == 1) {
-        const int small = config_by_name("128x128x64_s4_w2x4_m16");
+        const int small = config_by_name(a_window_pays(transa, transb, lda) ? "128x128x64_s4_w2x4_m16aw"
+                                                                            : "128x128x64_s4_w2x4_m16");
         bool cols = true;
         const int64_t cut = plan_retile(M, N, cus, &cols);
         if (cut > 0 && config_ok(kConfigs[small], transa, transb, vec, lda, ldb, ldc, c_type)) {
