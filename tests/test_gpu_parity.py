@@ -793,6 +793,35 @@ def test_a_window_choice(tdg):
     assert pick("nn", 4095, 5000, 3000, 3000) == "256x256x64_s2_w2x4_m16"
 
 
+# (layout, batch, M, N, K, lda, batch stride of A in elements): the batch
+# stride moves each problem's rows to another offset within the 128-byte
+# lines, so every problem of a call has its own row shifts.
+AWIN_BATCH_CASES = [("tn", 3, 300, 264, 1000, 1016, 1016 * 300 + 24),
+                    ("nn", 2, 257, 304, 520, 600, 600 * 257 + 8),
+                    ("tn", 2, 130, 97, 136, 200, 200 * 130 + 56)]
+
+
+@pytest.mark.parametrize("cfg", ["256x256x64_s2_w2x4_m16aw", "128x128x64_s4_w2x4_m16aw"])
+@pytest.mark.parametrize("layout,batch,M,N,K,lda,sa", AWIN_BATCH_CASES)
+def test_a_window_batched_exact(tdg, cfg, layout, batch, M, N, K, lda, sa):
+    """Both A-window configurations, forced, on batched products whose A
+    rows sit off the 128-byte lines by a shift that changes from problem to
+    problem, NaN in every byte around the rows: bit-exact against the
+    oracle problem by problem."""
+    announce("a window batched", cfg, layout, batch, M, N, K, lda, sa)
+    assert sa >= M * lda and (sa * 2) % 128 != 0
+    a, b = make_inputs(M, N, K, layout, "bf16", "ints", seed=batch + M + N + K, batch=batch)
+    pre = 64 + 8
+    store = torch.full((pre + (batch - 1) * sa + M * lda + 64,), float("nan"), dtype=torch.bfloat16)
+    store.as_strided((batch, M, K), (sa, lda, 1), pre).copy_(a)
+    sd = store.cuda()
+    assert sd.data_ptr() % 128 == 0
+    ad = sd.as_strided((batch, M, K), (sa, lda, 1), pre)
+    c = tdg.gemm(ad, b.cuda(), layout=layout, out_dtype=torch.float32, config=tdg.config_names().index(cfg))
+    torch.cuda.synchronize()
+    check_exact(c.cpu(), ref_gemm(a, b, "bf16", layout), "f32", "a window batched %s %s" % (cfg, layout))
+
+
 @pytest.mark.parametrize("M,N,K", [(512, 512, 16008), (4352, 4352, 1000), (4095, 5000, 3000)])
 def test_a_window_split_schedules_exact(tdg, M, N, K):
     """TN products with A rows off the 128-byte lines through the library's
