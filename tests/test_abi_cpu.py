@@ -121,11 +121,13 @@ def test_config_selection(tdg):
     assert sel(1, 8192, 8192, 8192) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 8192, 8192, 8192, c_type=2) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 4096, 4096, 4096) == "256x256x64_s2_w2x4_m16"
-    assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16"
-    # TN with A rows off the 128-byte lines: the A-window form
+    # A rows off the 128-byte lines: the A-window forms (256 x 256 for both
+    # layouts, 128 x 128 for TN only)
+    assert sel(0, 4095, 5000, 3000) == "256x256x64_s2_w2x4_m16aw"
+    assert sel(0, 4095, 5000, 3000, lda=3008) == "256x256x64_s2_w2x4_m16"
     assert sel(1, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16aw"
     assert sel(1, 4096, 4096, 3000, lda=3008) == "256x256x64_s2_w2x4_m16"
-    assert sel(0, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16"
+    assert sel(0, 4096, 4096, 3000) == "256x256x64_s2_w2x4_m16aw"
     assert sel(1, 1024, 1024, 3000) == "128x128x64_s4_w2x4_m16aw"
     assert sel(0, 1024, 1024, 3000) == "128x128x64_s4_w2x4_m16"
     # the persistent kernel: several rounds of 256 x 256 tiles and K <= 512
@@ -136,7 +138,8 @@ def test_config_selection(tdg):
     assert sel(1, 8192, 8192, 128, c_type=2) == "256x256x64_s2_w2x4_m16"       # fp32, single problem
     assert sel(1, 8192, 8192, 128) == "256x256x64_s2_w2x4_m16p"
     assert sel(0, 4096, 4096, 512, batch=4) == "256x256x64_s2_w2x4_m16p"
-    assert sel(0, 4096, 4096, 520, batch=4) == "256x256x64_s2_w2x4_m16"
+    assert sel(0, 4096, 4096, 520, lda=576, batch=4) == "256x256x64_s2_w2x4_m16"
+    assert sel(0, 4096, 4096, 520, batch=4) == "256x256x64_s2_w2x4_m16aw"   # lda 520: rows off the lines
     assert sel(1, 4096, 4096, 256) == "256x256x64_s2_w2x4_m16"          # a single round
     assert sel(0, 1024, 1024, 1024) == "128x128x64_s4_w2x4_m16"
     assert sel(0, 65, 97, 130).endswith("_pred")            # K not a multiple of 8

@@ -780,9 +780,10 @@ def test_a_window_exact(tdg, layout, M, N, K, lda, a_off, auto):
 
 
 def test_a_window_choice(tdg):
-    """The library picks the A-window form for TN products of at least one
-    round of 256 x 256 tiles whose A rows are off the 128-byte lines, and the
-    plain form for NN and for aligned rows."""
+    """The library picks the 256 x 256 A-window form for products of at
+    least one round of 256 x 256 tiles whose A rows are off the 128-byte
+    lines, in both layouts, the 128 x 128 one for smaller TN products only,
+    and the plain forms for aligned rows."""
     names = tdg.config_names()
     def pick(layout, M, N, K, lda):
         ad = torch.empty(M, lda, dtype=torch.float16, device="cuda")[:, :K]
@@ -790,7 +791,10 @@ def test_a_window_choice(tdg):
         return names[tdg.select_config(ad, bd, layout, torch.float16)]
     assert pick("tn", 4096, 4096, 3000, 3000).endswith("_m16aw")
     assert pick("tn", 4096, 4096, 3000, 3008) == "256x256x64_s2_w2x4_m16"
-    assert pick("nn", 4095, 5000, 3000, 3000) == "256x256x64_s2_w2x4_m16"
+    assert pick("nn", 4095, 5000, 3000, 3000) == "256x256x64_s2_w2x4_m16aw"
+    assert pick("nn", 4095, 5000, 3000, 3008) == "256x256x64_s2_w2x4_m16"
+    assert pick("tn", 1024, 1024, 3000, 3000) == "128x128x64_s4_w2x4_m16aw"
+    assert pick("nn", 1024, 1024, 3000, 3000) == "128x128x64_s4_w2x4_m16"
 
 
 # (layout, batch, M, N, K, lda, batch stride of A in elements): the batch

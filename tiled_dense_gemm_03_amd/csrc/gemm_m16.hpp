@@ -467,19 +467,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_m16_kernel(GemmArgs p) {
         // (lda is a multiple of 8) and depends on the row only modulo 8, so
         // every lane has one shift for its loads and one for its fragment
         // reads.  Elements before the row's first or past its K-th read as
-        // zeros.  LDS: A slot c % (STAGES + 1) (granule g of row r at
-        // g ^ kx16(r), as the other K-contiguous layouts), then the B stages.
+        // zeros.  LDS: A slot c % (STAGES + 1), then the B stages.  Within a
+        // chunk slot, granule g of row r (shift d = s / 16 granules) sits at
+        // ((g - d) & 7) ^ kx16(r): rotated by the row's shift, so that the
+        // granule a fragment read wants (4 ks + lane / 16 + d of the window,
+        // in chunk kt or kt + 1) is at (4 ks + lane / 16) ^ kx16(r) whatever
+        // d is -- the positions of the plain layout, whose reads do not
+        // conflict (unrotated, rows of different shifts put 25x the bank
+        // conflict cycles on the fragment reads).
         const char *Abytes = reinterpret_cast<const char *>(Atile);
         const int s_ld = (int)(((uintptr_t)Abytes + (uintptr_t)(kc_row * lda * 2)) & 127);
-        const int aw_e0 = 8 * kc_g - s_ld / 2;          // element of the lane's granule in chunk 0
-        const uint32_t aw_off = (uint32_t)(kc_row * lda * 2 + 16 * kc_g - s_ld + 128);
+        const int aw_g = (((lane % KG) ^ kxor<KG>(kc_row)) + (s_ld >> 4)) & 7;   // chunk granule this lane loads
+        const int aw_e0 = 8 * aw_g - s_ld / 2;          // element of the lane's granule in chunk 0
+        const uint32_t aw_off = (uint32_t)(kc_row * lda * 2 + 16 * aw_g - s_ld + 128);
         const int d_rd = (int)((((uintptr_t)Abytes + (uintptr_t)(fr * lda * 2)) & 127) >> 4);
         int aw_b[KS], aw_co[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int pp = 4 * ks + fg + d_rd;            // granule in the two-chunk window
-            aw_co[ks] = pp >> 3;
-            aw_b[ks] = (wave_m * WTM + fr) * KG + ((pp & 7) ^ kxor<KG>(fr));
+            aw_co[ks] = (4 * ks + fg + d_rd) >> 3;        // chunk kt or kt + 1
+            aw_b[ks] = (wave_m * WTM + fr) * KG + ((4 * ks + fg) ^ kxor<KG>(fr));
         }
         u32x4 *const bstages = smem + AW_R * A_SLOTS;
         auto dma_a = [&](auto qtag, int c) {              // A chunk c into slot c % AW_R

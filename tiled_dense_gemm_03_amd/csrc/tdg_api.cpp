@@ -142,13 +142,16 @@ int config_by_name(const char *name) {
     return -1;
 }
 
-// Whether a TN product's A rows start off the 128-byte lines (lda not a
-// multiple of 64 elements), where the A-window forms pay: measured against
-// the plain forms, TN 256 x 256 tiles 4-7% faster on five shapes and
-// 128 x 128 tiles 8% on two (both operands K-contiguous and off the lines);
-// NN within +-1.5% for 256 x 256 tiles and up to 12% slower for 128 x 128
-// tiles, so NN keeps the plain forms.
-bool a_window_pays(int transa, int transb, int64_t lda) { return transb && !transa && (lda * 2) % 128 != 0; }
+// Whether A's rows start off the 128-byte lines (A stored M x K, lda not a
+// multiple of 64 elements), where the A-window forms pay.  Measured against
+// the plain forms (same library, one box, bit-identical): 256 x 256 tiles
+// TN 7-8% faster (4096^2 x 3000, 8192^2 x 3000) and NN 1-1.5% (8192^2 x
+// 3000, the 4095 x 4096 band of 4095 x 5000 x 3000); 128 x 128 tiles TN 8%
+// faster on two shapes but NN 3-6% slower (1024^2 and 2048^2 x 3000), so the
+// 128 x 128 form is chosen for TN only (`big` selects the tile size).
+bool a_window_pays(int transa, int transb, int64_t lda, bool big) {
+    return !transa && (big || transb) && (lda * 2) % 128 != 0;
+}
 
 // Split-K schedule for the 16x16x32 kernel (NineToothed primer s4 names the
 // alternative to keeping K inside one program: split it, at the price of a
@@ -266,13 +269,13 @@ int choose(int transa, int transb, bool vec, int64_t M, int64_t N, int64_t K, in
         // kernel works out every row's shift from the actual addresses, so
         // this is only the choice; a_window_pays has the measurements)
         const int aw = config_by_name("256x256x64_s2_w2x4_m16aw");
-        if (tiles256 >= cus && a_window_pays(transa, transb, lda) &&
+        if (tiles256 >= cus && a_window_pays(transa, transb, lda, true) &&
             config_ok(kConfigs[aw], transa, transb, vec, lda, ldb, ldc, c_type))
             return aw;
         const int id = config_by_name("256x256x64_s2_w2x4_m16");
         if (tiles256 >= cus && config_ok(kConfigs[id], transa, transb, vec, lda, ldb, ldc, c_type)) return id;
         const int mid_aw = config_by_name("128x128x64_s4_w2x4_m16aw");
-        if (a_window_pays(transa, transb, lda) && config_ok(kConfigs[mid_aw], transa, transb, vec, lda, ldb, ldc, c_type))
+        if (a_window_pays(transa, transb, lda, false) && config_ok(kConfigs[mid_aw], transa, transb, vec, lda, ldb, ldc, c_type))
             return mid_aw;
         const int mid = config_by_name("128x128x64_s4_w2x4_m16");
         if (config_ok(kConfigs[mid], transa, transb, vec, lda, ldb, ldc, c_type)) return mid;
@@ -545,7 +548,7 @@ tdg_status run(int transa, int transb, int transc, int64_t M, int64_t N, int64_t
         }
     }
     if (automatic && !tuned && cf.kind >= 2 && batch == 1) {
-        const int small = config_by_name(a_window_pays(transa, transb, lda) ? "128x128x64_s4_w2x4_m16aw"
+        const int small = config_by_name(a_window_pays(transa, transb, lda, false) ? "128x128x64_s4_w2x4_m16aw"
                                                                             : "128x128x64_s4_w2x4_m16");
         bool cols = true;
         const int64_t cut = plan_retile(M, N, cus, &cols);
